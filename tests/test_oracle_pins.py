@@ -1,0 +1,363 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test names the part of the oracle it pins and what it is pinned to:
+hand-derived vectors (tests/golden/), a nearest-grid search, an exhaustive
+search, torch autograd, the Gram (H = XᵀX) identity, a library bf16 cast and
+big-integer packing.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def _cfg(**kw):
+    return O.Config(**kw)
+
+
+# ------------------------------------------------------------------ bf16
+def test_bf16_matches_library_cast():
+    """bf16() against torch's float32 -> bfloat16 cast (round to nearest even)."""
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal(200000).astype(F32) * F32(3.0)
+    # exact ties and edge values
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x7F7FFFFF, 0x00008000,
+                     0x00018000, 0x7F800000, 0xFF800000, 0x80000000, 0x00000001],
+                    dtype=np.uint32).view(F32)
+    x = np.concatenate([x, ties])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    got = O.bf16(x)
+    np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert np.isnan(O.bf16(np.array([np.nan], F32)))[0]
+
+
+# ------------------------------------------------------------------ S1
+def test_group_minmax_against_loops():
+    rng = np.random.default_rng(2)
+    W = rng.standard_normal((3, 24)).astype(F32)
+    mn, mx = O.group_minmax(W, 8)
+    for n in range(3):
+        for j in range(3):
+            vals = [float(W[n, j * 8 + i]) for i in range(8)]
+            assert mn[n, j] == min(vals) and mx[n, j] == max(vals)
+    mn, mx = O.group_minmax(W, -1)
+    assert mn.shape == (3, 1) and mx[1, 0] == W[1].max()
+
+
+# ------------------------------------------------------------------ S2, S3
+def _hand_cases():
+    with open(os.path.join(GOLDEN, "hand_vectors.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _hand_cases(), ids=lambda c: c["name"])
+def test_hand_vectors(case):
+    """qparams + fake_quant against hand-derived vectors (tests/golden)."""
+    W = np.array([case["W"]], F32)
+    V = np.array([case["V"]], F32)
+    g = case["group_size"]
+    wmin, wmax = O.group_minmax(W, g)
+    a = np.full(wmin.shape, F32(case["alpha"]))
+    b = np.full(wmin.shape, F32(case["beta"]))
+    qp = O.qparams(wmin, wmax, a, b, case["bits"], case["sym"])
+    assert qp.s[0, 0] == F32(case["s"])
+    assert qp.zp[0, 0] == case["zp"]
+    fq = O.fake_quant(W, V, qp, case["bits"], g)
+    np.testing.assert_array_equal(fq.q[0].astype(int), case["codes"])
+    np.testing.assert_array_equal(fq.m[0].astype(int), case["mask"])
+    np.testing.assert_array_equal(fq.what[0], np.array(case["what"], F32))
+
+
+@pytest.mark.parametrize("bits,sym", [(2, False), (3, False), (4, False), (8, False),
+                                      (2, True), (3, True), (4, True), (8, True)])
+def test_rtn_is_nearest_grid_point(bits, sym):
+    """With V = 0 and alpha = beta = 1 each code is the grid point nearest to
+    W (the RTN equation), found here by searching every code q in [0, maxq]."""
+    rng = np.random.default_rng(bits * 10 + sym)
+    N, K, g = 16, 64, 16
+    W = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    W[3, :16] = np.abs(W[3, :16])          # an all-positive group
+    W[5, 16:32] = -np.abs(W[5, 16:32])     # an all-negative group
+    cfg = _cfg(bits=bits, sym=sym, group_size=g)
+    codes, s, zp, what = O.rtn_quant(W, cfg)
+    maxq = 2 ** bits - 1
+    assert codes.max() <= maxq and zp.max() <= maxq
+    s_e = np.repeat(s, g, axis=1).astype(np.float64)
+    zp_e = np.repeat(zp, g, axis=1).astype(np.float64)
+    grid = s_e[..., None] * (np.arange(maxq + 1)[None, None, :] - zp_e[..., None])
+    dist = np.abs(grid - W.astype(np.float64)[..., None])
+    nearest = dist.argmin(axis=2)
+    t64 = W.astype(np.float64) / s_e
+    frac = np.abs(t64 - np.floor(t64) - 0.5)
+    clear = frac > 1e-5                   # away from exact halves
+    np.testing.assert_array_equal(codes[clear], nearest[clear])
+    # |what - W| <= s/2 in range
+    err = np.abs(what.astype(np.float64) - W.astype(np.float64))
+    inrange = (np.abs(t64 + zp_e - np.clip(t64 + zp_e, 0, maxq)) == 0) & clear
+    assert np.all(err[inrange] <= s_e[inrange] * 0.5 * (1 + 1e-6))
+
+
+def test_codes_and_offsets_stay_in_range():
+    rng = np.random.default_rng(3)
+    N, K, g = 8, 128, 32
+    W = (rng.standard_normal((N, K)) * 0.05).astype(F32)
+    V = rng.uniform(-0.5, 0.5, (N, K)).astype(F32)
+    for bits in O.SUPPORTED_BITS:
+        for sym in (False, True):
+            wmin, wmax = O.group_minmax(W, g)
+            a = rng.uniform(0.5, 1.0, wmin.shape).astype(F32)
+            b = rng.uniform(0.5, 1.0, wmin.shape).astype(F32)
+            qp = O.qparams(wmin, wmax, a, b, bits, sym)
+            fq = O.fake_quant(W, V, qp, bits, g)
+            assert fq.q.min() >= 0 and fq.q.max() <= 2 ** bits - 1
+            assert qp.zp.min() >= 0 and qp.zp.max() <= 2 ** bits - 1
+            assert np.all(qp.s > 0)
+
+
+def test_offset_zero_reproduces_rint():
+    """V = 0 turns the offset equation into the RTN equation."""
+    rng = np.random.default_rng(4)
+    W = (rng.standard_normal((4, 64)) * 0.02).astype(F32)
+    wmin, wmax = O.group_minmax(W, 16)
+    one = np.ones_like(wmin)
+    qp = O.qparams(wmin, wmax, one, one, 4, False)
+    fq = O.fake_quant(W, np.zeros_like(W), qp, 4, 16)
+    s_e = np.repeat(qp.s, 16, axis=1)
+    zp_e = np.repeat(qp.zp, 16, axis=1)
+    np.testing.assert_array_equal(fq.q, np.clip(np.rint(W / s_e) + zp_e, 0, 15))
+
+
+# ------------------------------------------------------------------ S4-S7
+def _problem(N=6, K=32, T=40, seed=5, sym=False, bits=3, g=8):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    W[0, :g] = np.abs(W[0, :g]) + F32(0.001)   # all-positive group
+    X = rng.standard_normal((T, K))
+    Y = X @ W.astype(np.float64).T
+    wmin, wmax = O.group_minmax(W, g)
+    a = rng.uniform(0.6, 1.0, wmin.shape).astype(F32)
+    b = rng.uniform(0.6, 1.0, wmin.shape).astype(F32)
+    V = rng.uniform(-0.5, 0.5, (N, K)).astype(F32)
+    return W, X, Y, wmin, wmax, a, b, V
+
+
+def test_loss_and_grad_gram_identity():
+    """Exact mode: L = Tr(ΔW·H·ΔWᵀ)/(T·N) and G = 2·ΔW·H/(T·N) with H = XᵀX
+    (the Hessian form of the layer objective on the ADMM-Q page)."""
+    W, X, Y, wmin, wmax, a, b, V = _problem()
+    qp = O.qparams(wmin, wmax, a, b, 3, False)
+    fq = O.fake_quant(W, V, qp, 3, 8)
+    L, G, _ = O.forward_backward(X, Y, fq.what, amp=False)
+    T, N = X.shape[0], W.shape[0]
+    dW = fq.what.astype(np.float64) - W.astype(np.float64)
+    H = X.T @ X
+    np.testing.assert_allclose(L, np.trace(dW @ H @ dW.T) / (T * N), rtol=1e-10)
+    np.testing.assert_allclose(G, 2.0 * dW @ H / (T * N), rtol=1e-9, atol=1e-15)
+
+
+def test_amp_close_to_exact():
+    W, X, Y, wmin, wmax, a, b, V = _problem(K=64, T=64)
+    qp = O.qparams(wmin, wmax, a, b, 3, False)
+    fq = O.fake_quant(W, V, qp, 3, 8)
+    Xb = O.bf16(X.astype(F32))
+    L1, G1, _ = O.forward_backward(Xb, Y, fq.what, amp=True)
+    L2, G2, _ = O.forward_backward(Xb, Y, fq.what, amp=False)
+    assert abs(L1 - L2) / L2 < 2e-2
+    assert np.linalg.norm(G1 - G2) / np.linalg.norm(G2) < 5e-2
+
+
+# ------------------------------------------------------------------ S8
+def _autograd_grads(W, X, Y, wmin, wmax, a, b, V, bits, sym, g):
+    """The same forward in torch float64 with a straight-through rint
+    (x + (round(x) - x).detach()); gradients by autograd."""
+    d = torch.float64
+    Wt = torch.tensor(W, dtype=d)
+    Vt = torch.tensor(V, dtype=d, requires_grad=True)
+    at = torch.tensor(a, dtype=d, requires_grad=True)
+    bt = torch.tensor(b, dtype=d, requires_grad=True)
+    mn = torch.tensor(wmin, dtype=d)
+    mx = torch.tensor(wmax, dtype=d)
+    maxq = 2 ** bits - 1
+
+    def rint_ste(x):
+        return x + (torch.round(x) - x).detach()
+
+    if sym:
+        amax = torch.maximum((at * mn).abs(), (bt * mx).abs())
+        s = 2 * amax / maxq
+        s = torch.where(s == 0, torch.ones_like(s), s)
+        zp = torch.full_like(s, 2 ** (bits - 1))
+    else:
+        lo = torch.minimum(at * mn, torch.zeros_like(mn))
+        hi = torch.maximum(bt * mx, torch.zeros_like(mx))
+        s = (hi - lo) / maxq
+        s = torch.where(s == 0, torch.ones_like(s), s)
+        zp = torch.clamp(rint_ste(-lo / s), 0, maxq)
+    s_e = s.repeat_interleave(g, dim=1)
+    zp_e = zp.repeat_interleave(g, dim=1)
+    q = torch.clamp(rint_ste(Wt / s_e + Vt) + zp_e, 0, maxq)
+    what = s_e * (q - zp_e)
+    Yp = torch.tensor(X, dtype=d) @ what.T
+    L = ((Yp - torch.tensor(Y, dtype=d)) ** 2).mean()
+    L.backward()
+    return Vt.grad.numpy(), at.grad.numpy(), bt.grad.numpy()
+
+
+@pytest.mark.parametrize("sym,bits", [(False, 2), (False, 3), (False, 4), (True, 3), (True, 4)])
+def test_ste_grads_match_autograd(sym, bits):
+    W, X, Y, wmin, wmax, a, b, V = _problem(seed=10 + bits, sym=sym, bits=bits)
+    g = 8
+    qp = O.qparams(wmin, wmax, a, b, bits, sym)
+    fq = O.fake_quant(W, V, qp, bits, g)
+    L, G, _ = O.forward_backward(X, Y, fq.what, amp=False)
+    gV, ga, gb = O.ste_grads(G, W, fq, qp, wmin, wmax, a, b, bits, sym, g)
+    rV, ra, rb = _autograd_grads(W, X, Y, wmin, wmax, a, b, V, bits, sym, g)
+    # float32 (oracle) vs float64 (autograd) forward: agreement to ~1e-5; a
+    # wrong sign or a dropped term would be an O(1) difference.
+    np.testing.assert_allclose(gV, rV, rtol=1e-4, atol=1e-6 * np.abs(rV).max())
+    np.testing.assert_allclose(ga, ra, rtol=1e-4, atol=1e-6 * np.abs(ra).max())
+    np.testing.assert_allclose(gb, rb, rtol=1e-4, atol=1e-6 * np.abs(rb).max())
+    assert np.abs(ga).max() > 0 and np.abs(gb).max() > 0
+
+
+# ------------------------------------------------------------------ S9
+def test_signsgd_update_invariants():
+    rng = np.random.default_rng(7)
+    cfg = _cfg(lr=0.005, minmax_lr=0.01)
+    V = rng.uniform(-0.5, 0.5, (4, 64)).astype(F32)
+    V[0, :4] = [0.5, -0.5, 0.498, 0.0]
+    gV = rng.standard_normal((4, 64))
+    gV[0, :4] = [-1.0, 1.0, -1.0, 0.0]
+    a = np.array([[1.0, 0.5, 0.75, 0.7]], F32)
+    ga = np.array([[-1.0, 1.0, 0.0, 2.0]])
+    Vn, an, bn = O.signsgd_update(V, a, a, gV, ga, -ga, cfg)
+    assert Vn.min() >= -0.5 and Vn.max() <= 0.5
+    np.testing.assert_array_equal(Vn[0, :4], np.array([0.5, -0.5, 0.5, 0.0], F32))
+    dV = Vn.astype(np.float64) - V
+    assert np.all(dV * gV <= 0)                       # against the gradient
+    assert np.all(np.abs(dV) <= 0.005 * (1 + 1e-6))
+    np.testing.assert_array_equal(an[0], np.array([1.0, 0.5, 0.75, F32(0.7) - F32(0.01)], F32))
+    np.testing.assert_array_equal(bn[0], np.array([F32(1.0) - F32(0.01), F32(0.5) + F32(0.01),
+                                                   0.75, F32(0.7) + F32(0.01)], F32))
+
+
+# ------------------------------------------------------------------ whole loop
+def _full_batch_problem(N=4, K=32, T=64, g=16, seed=11):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    X = O.bf16(rng.standard_normal((T, K)).astype(F32))
+    Y = (X.astype(np.float64) @ W.astype(np.float64).T).astype(F32)
+    return W, X, Y
+
+
+def test_iters_zero_is_rtn():
+    """Zero iterations give the RTN result (Introducing AutoRound page,
+    section 4)."""
+    W, X, Y = _full_batch_problem()
+    cfg = _cfg(bits=4, group_size=16, iters=0)
+    r = O.tune_linear(W, lambda b: (X, Y), 1, cfg)
+    codes, s, zp, what = O.rtn_quant(W, cfg)
+    np.testing.assert_array_equal(r.codes, codes)
+    np.testing.assert_array_equal(r.zp, zp)
+    np.testing.assert_array_equal(r.scale, s)
+    assert r.losses == [] and r.best_step == -1
+
+
+def test_best_snapshot_not_worse_than_rtn():
+    """Full batch: the returned state is the best evaluated one, so its loss
+    equals best_loss and is not above the RTN loss (the first evaluated)."""
+    W, X, Y = _full_batch_problem()
+    for bits in (2, 3, 4):
+        cfg = _cfg(bits=bits, group_size=16, iters=25)
+        r = O.tune_linear(W, lambda b: (X, Y), 1, cfg)
+        assert r.best_loss <= r.losses[0]
+        assert r.best_loss == min(r.losses)
+        wmin, wmax = O.group_minmax(W, 16)
+        qp = O.qparams(wmin, wmax, r.alpha, r.beta, bits, False)
+        fq = O.fake_quant(W, r.V, qp, bits, 16)
+        L, _, _ = O.forward_backward(X, Y, fq.what)
+        assert L == r.best_loss
+        assert r.V.min() >= -0.5 and r.V.max() <= 0.5
+        assert r.alpha.min() >= 0.5 and r.beta.max() <= 1.0
+
+
+def test_brute_force_2x4():
+    """2x4 weight, 2-bit asym, one group per row, s and zp frozen
+    (minmax_lr = 0), exact arithmetic: neither RTN nor 200 SignSGD steps can
+    beat the exhaustive optimum over all 2^8 up/down roundings."""
+    rng = np.random.default_rng(0)
+    W = (rng.normal(0.0, 0.02, (2, 4))).astype(F32)
+    X = rng.standard_normal((16, 4))
+    Y = X @ W.astype(np.float64).T
+    cfg = _cfg(bits=2, group_size=4, iters=200, minmax_lr=0.0)
+    wmin, wmax = O.group_minmax(W, 4)
+    one = np.ones_like(wmin)
+    qp = O.qparams(wmin, wmax, one, one, 2, False)
+    t = W / np.repeat(qp.s, 4, axis=1)
+    assert np.all(np.abs(t - np.floor(t) - 0.5) > 1e-3)   # generic t
+    best_rows, best_codes = O.brute_force_rounding(W, X, Y, qp, 2, 4)
+
+    def row_losses(codes):
+        w_hat = np.repeat(qp.s, 4, axis=1).astype(np.float64) * \
+            (codes.astype(np.float64) - np.repeat(qp.zp, 4, axis=1))
+        return np.sum((X @ w_hat.T - Y) ** 2, axis=0)
+
+    rtn_codes, _, _, _ = O.rtn_quant(W, cfg)
+    r = O.tune_linear(W, lambda b: (X, Y), 1, cfg, amp=False)
+    np.testing.assert_array_equal(r.scale, qp.s)
+    assert np.all(row_losses(rtn_codes) >= best_rows - 1e-12)
+    assert np.all(row_losses(r.codes) >= best_rows - 1e-12)
+    assert row_losses(r.codes).sum() <= row_losses(rtn_codes).sum() + 1e-15
+
+
+# ------------------------------------------------------------------ S11
+def _pack_cases():
+    with open(os.path.join(GOLDEN, "pack_vectors.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _pack_cases(), ids=lambda c: f"b{c['bits']}")
+def test_pack_hand_words(case):
+    bits = case["bits"]
+    if "codes" in case:
+        codes = np.array(case["codes"], np.uint8)
+    else:
+        codes = np.full(case["length"], case.get("codes_fill", 0), np.uint8)
+        for k, v in case.get("codes_sparse", {}).items():
+            codes[int(k)] = v
+    qw = O._pack_axis0(codes[:, None], bits)
+    assert [int(w) for w in qw[:, 0]] == [int(w, 16) for w in case["words"]]
+    np.testing.assert_array_equal(O._unpack_axis0(qw, bits, len(codes))[:, 0], codes)
+
+
+@pytest.mark.parametrize("bits", O.SUPPORTED_BITS)
+def test_pack_matches_bigint_and_roundtrips(bits):
+    """Packing against a Python big-integer bit string built per column."""
+    rng = np.random.default_rng(bits)
+    N, K, g = 32, 96, 32
+    codes = rng.integers(0, 2 ** bits, (N, K), dtype=np.uint8)
+    zp = rng.integers(0, 2 ** bits, (N, K // g), dtype=np.uint8)
+    qw, qz = O.pack(codes, zp, bits)
+    assert qw.shape == (K * bits // 32, N) and qz.shape == (K // g, N * bits // 32)
+    for n in range(N):
+        acc = 0
+        for k in range(K):
+            acc |= int(codes[n, k]) << (k * bits)
+        words = [(acc >> (32 * w)) & 0xFFFFFFFF for w in range(K * bits // 32)]
+        assert [int(x) for x in qw[:, n]] == words
+    for j in range(K // g):
+        acc = 0
+        for n in range(N):
+            acc |= int(zp[n, j]) << (n * bits)
+        assert [int(x) for x in qz[j]] == [(acc >> (32 * w)) & 0xFFFFFFFF
+                                           for w in range(N * bits // 32)]
+    c2, z2 = O.unpack(qw, qz, bits, N, K)
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_array_equal(z2, zp)
