@@ -1,0 +1,314 @@
+"""Python binding of libautoround_hip.so (AutoRound per-Linear tuning on gfx950).
+
+Argument marshalling only: torch tensors provide device memory and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+Importing this package loads the library and fails loudly if it is missing.
+Entry points mirror include/autoround_hip.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libautoround_hip.so")
+
+AR_F32, AR_BF16 = 0, 1
+SUPPORTED_BITS = (2, 3, 4, 8)
+
+STATUS = {
+    0: "AR_OK", 1: "AR_ERR_INVALID_ARG", 2: "AR_ERR_UNSUPPORTED", 3: "AR_ERR_SHAPE",
+    4: "AR_ERR_WORKSPACE", 6: "AR_ERR_HIP",
+}
+
+# every symbol declared in include/autoround_hip.h
+EXPORTS = (
+    "ar_config_default", "ar_status_string", "ar_workspace_size", "ar_step_workspace_size",
+    "ar_rtn_quant", "ar_fakequant_fwd", "ar_tune_step", "ar_tune_linear", "ar_pack", "ar_unpack",
+)
+
+
+class ArConfig(ctypes.Structure):
+    _fields_ = [
+        ("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("sym", ctypes.c_int32),
+        ("nsamples", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+        ("batch_samples", ctypes.c_int32), ("iters", ctypes.c_int32),
+        ("lr", ctypes.c_float), ("minmax_lr", ctypes.c_float),
+        ("minmax_shrink", ctypes.c_float), ("clip_lo", ctypes.c_float),
+        ("clip_hi", ctypes.c_float),
+    ]
+
+
+class ArState(ctypes.Structure):
+    _fields_ = [
+        ("W", ctypes.c_void_p), ("wdt", ctypes.c_int32), ("N", ctypes.c_int64),
+        ("K", ctypes.c_int64), ("V", ctypes.c_void_p), ("alpha", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p), ("best_V", ctypes.c_void_p),
+        ("best_alpha", ctypes.c_void_p), ("best_beta", ctypes.c_void_p),
+        ("best_loss", ctypes.c_void_p),
+    ]
+
+
+class ArKernelTimes(ctypes.Structure):
+    _fields_ = [
+        ("fwd_gemm_ms", ctypes.c_double), ("wgrad_gemm_ms", ctypes.c_double),
+        ("ste_update_ms", ctypes.c_double), ("loss_ms", ctypes.c_double),
+        ("steps", ctypes.c_int64),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m autoround_signsgd_rounding_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cfgp = ctypes.POINTER(ArConfig)
+    sig = {
+        "ar_config_default": [cfgp],
+        "ar_workspace_size": [cfgp, i64, i64, i32, ctypes.POINTER(sz)],
+        "ar_step_workspace_size": [cfgp, i64, i64, i64, i32, ctypes.POINTER(sz)],
+        "ar_rtn_quant": [cfgp, i32, vp, i64, i64, vp, vp, vp, vp, vp],
+        "ar_fakequant_fwd": [cfgp, i32, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp],
+        "ar_tune_step": [cfgp, ctypes.POINTER(ArState), vp, vp, i32, i64, vp, vp, vp, vp, i32,
+                         vp, sz, vp],
+        "ar_tune_linear": [cfgp, i32, vp, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                           vp, sz, ctypes.POINTER(ArKernelTimes), vp],
+        "ar_pack": [i32, vp, vp, i64, i64, i64, vp, vp, vp],
+        "ar_unpack": [i32, vp, vp, i64, i64, i64, vp, vp, vp],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int32
+    lib.ar_status_string.argtypes = [ctypes.c_int32]
+    lib.ar_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+class ArError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.ar_status_string(status).decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({msg})")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise ArError(status, where)
+
+
+@dataclasses.dataclass
+class Config:
+    """Tuning hyper-parameters (names of the llm-compressor AutoRoundModifier)."""
+    bits: int = 4
+    group_size: int = 128
+    sym: bool = False
+    nsamples: int = 128
+    seqlen: int = 2048
+    batch_samples: int = 8
+    iters: int = 200
+    lr: float = 0.005
+    minmax_lr: float | None = None
+    minmax_shrink: float = 1.0
+    clip_lo: float = 0.5
+    clip_hi: float = 1.0
+
+    def c(self) -> ArConfig:
+        return ArConfig(self.bits, self.group_size, int(self.sym), self.nsamples, self.seqlen,
+                        self.batch_samples, self.iters, self.lr,
+                        -1.0 if self.minmax_lr is None else self.minmax_lr,
+                        self.minmax_shrink, self.clip_lo, self.clip_hi)
+
+    def G(self, K: int) -> int:
+        return 1 if self.group_size == -1 else K // self.group_size
+
+
+# ------------------------------------------------------------------ torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return AR_F32
+    if t.dtype == torch.bfloat16:
+        return AR_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def workspace_size(cfg: Config, N: int, K: int, ydtype) -> int:
+    out = ctypes.c_size_t()
+    cc = cfg.c()
+    _check(lib.ar_workspace_size(ctypes.byref(cc), N, K, ydtype, ctypes.byref(out)),
+           "ar_workspace_size")
+    return out.value
+
+
+def step_workspace_size(cfg: Config, N: int, K: int, Tb: int, ydtype) -> int:
+    out = ctypes.c_size_t()
+    cc = cfg.c()
+    _check(lib.ar_step_workspace_size(ctypes.byref(cc), N, K, Tb, ydtype, ctypes.byref(out)),
+           "ar_step_workspace_size")
+    return out.value
+
+
+def rtn_quant(W, cfg: Config, stream=None, want_wq: bool = True):
+    """RTN codes [N,K] u8, scale [N,G] f32, zp [N,G] u8, Wq [N,K] (W's dtype)."""
+    torch = _torch()
+    _dev(W)
+    N, K = W.shape
+    G = cfg.G(K)
+    codes = torch.empty((N, K), dtype=torch.uint8, device=W.device)
+    scale = torch.empty((N, G), dtype=torch.float32, device=W.device)
+    zp = torch.empty((N, G), dtype=torch.uint8, device=W.device)
+    Wq = torch.empty_like(W) if want_wq else None
+    cc = cfg.c()
+    _check(lib.ar_rtn_quant(ctypes.byref(cc), _dt(W), _ptr(W), N, K, _ptr(codes), _ptr(scale),
+                            _ptr(zp), _ptr(Wq), _stream(stream)), "ar_rtn_quant")
+    return codes, scale, zp, Wq
+
+
+def fakequant_fwd(W, V, alpha, beta, cfg: Config, stream=None):
+    """bf16 Ŵ [N,K], codes [N,K] u8, scale [N,G] f32, zp [N,G] u8."""
+    torch = _torch()
+    _dev(W, V, alpha, beta)
+    N, K = W.shape
+    G = cfg.G(K)
+    Wq = torch.empty((N, K), dtype=torch.bfloat16, device=W.device)
+    codes = torch.empty((N, K), dtype=torch.uint8, device=W.device)
+    scale = torch.empty((N, G), dtype=torch.float32, device=W.device)
+    zp = torch.empty((N, G), dtype=torch.uint8, device=W.device)
+    cc = cfg.c()
+    _check(lib.ar_fakequant_fwd(ctypes.byref(cc), _dt(W), _ptr(W), N, K, _ptr(V), _ptr(alpha),
+                                _ptr(beta), _ptr(Wq), _ptr(codes), _ptr(scale), _ptr(zp),
+                                _stream(stream)), "ar_fakequant_fwd")
+    return Wq, codes, scale, zp
+
+
+def tune_step(W, V, alpha, beta, Xb, Yb, cfg: Config, *, best=None, want_grads=True,
+              apply_update=True, workspace=None, stream=None):
+    """One SignSGD step in place on (V, alpha, beta). ``best`` is an optional
+    tuple (best_V, best_alpha, best_beta, best_loss[1]). Returns
+    (loss[1] device tensor, gV, galpha, gbeta) with grads None unless wanted."""
+    torch = _torch()
+    _dev(W, V, alpha, beta, Xb, Yb)
+    N, K = W.shape
+    Tb = Xb.shape[0]
+    if Xb.dtype != torch.bfloat16 or Xb.shape[1] != K or tuple(Yb.shape) != (Tb, N):
+        raise ValueError("Xb must be bf16 [Tb, K] and Yb [Tb, N]")
+    ydt = _dt(Yb)
+    if workspace is None:
+        workspace = torch.empty(step_workspace_size(cfg, N, K, Tb, ydt), dtype=torch.uint8,
+                                device=W.device)
+    loss = torch.empty(1, dtype=torch.float32, device=W.device)
+    gV = torch.empty_like(V) if want_grads else None
+    ga = torch.empty_like(alpha) if want_grads else None
+    gb = torch.empty_like(beta) if want_grads else None
+    bV, bA, bB, bL = best if best is not None else (None, None, None, None)
+    st = ArState(W.data_ptr(), _dt(W), N, K, V.data_ptr(), alpha.data_ptr(), beta.data_ptr(),
+                 None if bV is None else bV.data_ptr(), None if bA is None else bA.data_ptr(),
+                 None if bB is None else bB.data_ptr(), None if bL is None else bL.data_ptr())
+    cc = cfg.c()
+    _check(lib.ar_tune_step(ctypes.byref(cc), ctypes.byref(st), _ptr(Xb), _ptr(Yb), ydt, Tb,
+                            _ptr(loss), _ptr(gV), _ptr(ga), _ptr(gb), int(apply_update),
+                            _ptr(workspace), workspace.numel(), _stream(stream)), "ar_tune_step")
+    return loss, gV, ga, gb
+
+
+@dataclasses.dataclass
+class TuneOutput:
+    codes: object
+    scale: object
+    zp: object
+    Wq: object
+    V: object
+    alpha: object
+    beta: object
+    losses: object
+    times: ArKernelTimes | None
+
+
+def tune_linear(W, X, Y, cfg: Config, *, want_state=True, want_wq=False, timed=False,
+                workspace=None, stream=None) -> TuneOutput:
+    """The whole tuning loop of one Linear (X [nsamples*seqlen, K] bf16,
+    Y [nsamples*seqlen, N] bf16/f32)."""
+    torch = _torch()
+    _dev(W, X, Y)
+    N, K = W.shape
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bf16")
+    G = cfg.G(K)
+    ydt = _dt(Y)
+    dev = W.device
+    if workspace is None:
+        workspace = torch.empty(workspace_size(cfg, N, K, ydt), dtype=torch.uint8, device=dev)
+    codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    scale = torch.empty((N, G), dtype=torch.float32, device=dev)
+    zp = torch.empty((N, G), dtype=torch.uint8, device=dev)
+    Wq = torch.empty_like(W) if want_wq else None
+    V = torch.empty((N, K), dtype=torch.float32, device=dev) if want_state else None
+    a = torch.empty((N, G), dtype=torch.float32, device=dev) if want_state else None
+    b = torch.empty((N, G), dtype=torch.float32, device=dev) if want_state else None
+    losses = torch.empty(max(cfg.iters, 1), dtype=torch.float32, device=dev)
+    times = ArKernelTimes() if timed else None
+    cc = cfg.c()
+    _check(lib.ar_tune_linear(ctypes.byref(cc), _dt(W), _ptr(W), N, K, _ptr(X), _ptr(Y), ydt,
+                              _ptr(codes), _ptr(scale), _ptr(zp), _ptr(Wq), _ptr(V), _ptr(a),
+                              _ptr(b), _ptr(losses), _ptr(workspace), workspace.numel(),
+                              ctypes.byref(times) if timed else None, _stream(stream)),
+           "ar_tune_linear")
+    return TuneOutput(codes, scale, zp, Wq, V, a, b, losses[:cfg.iters], times)
+
+
+def pack(codes, zp, bits: int, stream=None):
+    """qweight [K*bits/32, N] int32 and qzeros [G, N*bits/32] int32 (or None)."""
+    torch = _torch()
+    _dev(codes, zp)
+    N, K = codes.shape
+    qw = torch.empty((K * bits // 32, N), dtype=torch.int32, device=codes.device)
+    qz = None
+    G = 0
+    if zp is not None:
+        G = zp.shape[1]
+        qz = torch.empty((G, N * bits // 32), dtype=torch.int32, device=codes.device)
+    _check(lib.ar_pack(bits, _ptr(codes), _ptr(zp), N, K, G, _ptr(qw), _ptr(qz),
+                       _stream(stream)), "ar_pack")
+    return qw, qz
+
+
+def unpack(qweight, qzeros, bits: int, N: int, K: int, G: int, stream=None):
+    torch = _torch()
+    _dev(qweight, qzeros)
+    codes = torch.empty((N, K), dtype=torch.uint8, device=qweight.device)
+    zp = torch.empty((N, G), dtype=torch.uint8, device=qweight.device) if qzeros is not None \
+        else None
+    _check(lib.ar_unpack(bits, _ptr(qweight), _ptr(qzeros), N, K, G, _ptr(codes), _ptr(zp),
+                         _stream(stream)), "ar_unpack")
+    return codes, zp

@@ -1,0 +1,541 @@
+// Quantizer-side kernels of the tuning step (gfx950): fake-quant, the
+// straight-through fold + SignSGD update, loss finalisation, transposes and
+// int32 packing. All HBM-bound; every group of g contiguous input channels of
+// one output row is handled by LPG consecutive lanes, each lane streaming
+// 8-element chunks (16 B of bf16 / 32 B of float32) so that a wave reads
+// contiguous, coalesced spans.
+//
+// Sources: llm-compressor AutoRound page (paper-core equations for RTN, the
+// learnable offset and SignSGD; _fake_quantize_with_offset; the per-module
+// tuning loop), Introducing AutoRound page section 2 (clip range tuned with
+// the rounding), SGLang AutoRound page "1. AutoRoundConfig" (pack_factor).
+#include <math.h>
+
+#include "ar_device.h"
+#include "ar_launch.h"
+
+void ar_group_layout(int g, int* lpg, int* chunks_per_lane) {
+  const int chunks = g / 8;
+  int l = 1;
+  while (l < 64 && chunks % (2 * l) == 0) l *= 2;
+  *lpg = l;
+  *chunks_per_lane = chunks / l;
+}
+
+namespace {
+
+constexpr int NT = 256;
+
+__device__ __forceinline__ Grid grid_of(const ArGrid& g) { return Grid{g.maxq, g.half, g.sym}; }
+
+// ------------------------------------------------------------------ fake-quant
+template <typename WT, typename OT>
+struct FQArgs {
+  const WT* W;
+  const float* V;
+  const float* alpha;
+  const float* beta;
+  float shrink;
+  int64_t ngroups, K;
+  int g, Gn, E;
+  ArGrid gr;
+  OT* Wq;
+  uint8_t* codes;
+  float* scale;
+  uint8_t* zp;
+};
+
+template <typename WT, typename OT, int LPG>
+__global__ __launch_bounds__(NT) void k_fakequant(FQArgs<WT, OT> a) {
+  const int64_t gid = ((int64_t)blockIdx.x * NT + threadIdx.x) / LPG;
+  const int lig = threadIdx.x % LPG;
+  if (gid >= a.ngroups) return;
+  const Grid gr = grid_of(a.gr);
+  const int64_t n = gid / a.Gn;
+  const int64_t base = n * a.K + (gid - n * a.Gn) * a.g;
+
+  float mn = INFINITY, mx = -INFINITY;
+  for (int e = 0; e < a.E; ++e) {
+    float w[8];
+    load8(a.W + base + 8 * (lig + LPG * e), w);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { mn = fminf(mn, w[i]); mx = fmaxf(mx, w[i]); }
+  }
+  mn = group_min<LPG>(mn);
+  mx = group_max<LPG>(mx);
+  const float al = a.alpha ? a.alpha[gid] : a.shrink;
+  const float be = a.beta ? a.beta[gid] : a.shrink;
+  const QP p = group_qparams(mn, mx, al, be, gr);
+  if (lig == 0) {
+    if (a.scale) a.scale[gid] = p.s;
+    if (a.zp) a.zp[gid] = (uint8_t)(int)p.zp;
+  }
+  for (int e = 0; e < a.E; ++e) {
+    const int64_t off = base + 8 * (lig + LPG * e);
+    float w[8], v[8], q[8], wh[8];
+    load8(a.W + off, w);
+    if (a.V) {
+      load8(a.V + off, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const QE qe = quant_elem(w[i], v[i], p, gr);
+      q[i] = qe.q;
+      wh[i] = qe.what;
+    }
+    if (a.Wq) store8(a.Wq + off, wh);
+    if (a.codes) store8_u8(a.codes + off, q);
+  }
+}
+
+// ------------------------------------------------------------------ STE + SignSGD
+template <typename WT>
+struct SteK {
+  const WT* W;
+  float* V;
+  float* alpha;
+  float* beta;
+  const float* G;
+  int64_t ngroups, K;
+  int g, Gn, E;
+  ArGrid gr;
+  float lr, mlr, clip_lo, clip_hi;
+  const int* flag;
+  float* bestV;
+  float* bestA;
+  float* bestB;
+  float* gV;
+  float* gA;
+  float* gB;
+  int apply;
+  uint16_t* Wq_next;
+};
+
+// Straight-through sums of one chunk: A += G·((q - zp) - m·t), Bs += G·[not m].
+__device__ __forceinline__ void ste_accum(const float (&w)[8], const float (&v)[8],
+                                          const float (&g)[8], const QP& p, const Grid& gr,
+                                          float& A, float& Bs) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const QE e = quant_elem(w[i], v[i], p, gr);
+    const float d = (e.q - p.zp) - (e.m ? e.t : 0.0f);
+    A += g[i] * d;
+    if (!e.m) Bs += g[i];
+  }
+}
+
+// One step for the elements of one chunk: dL/dV = G·s·m, optional snapshot of
+// the pre-update offset, V <- clamp(V - lr·sgn(dL/dV), -0.5, 0.5), and the bf16
+// fake-quant of the updated state for the next forward product.
+template <typename WT>
+__device__ __forceinline__ void ste_finish(const SteK<WT>& a, int64_t off, const float (&w)[8],
+                                           const float (&v)[8], const float (&g)[8], const QP& p,
+                                           const QP& pn, const Grid& gr, bool snap) {
+  float gv[8], vn[8], wq[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const QE e = quant_elem(w[i], v[i], p, gr);
+    gv[i] = e.m ? g[i] * p.s : 0.0f;
+    const float sg = e.m ? sgnf(g[i]) : 0.0f;
+    vn[i] = a.apply ? fminf(fmaxf(v[i] - a.lr * sg, -0.5f), 0.5f) : v[i];
+    wq[i] = quant_elem(w[i], vn[i], pn, gr).what;
+  }
+  if (a.gV) store8(a.gV + off, gv);
+  if (snap) store8(a.bestV + off, v);
+  if (a.apply) store8(a.V + off, vn);
+  if (a.Wq_next) store8(a.Wq_next + off, wq);
+}
+
+// ONE: each lane holds exactly one chunk of its group (kept in registers
+// across the three phases); otherwise chunks are re-read per phase.
+template <typename WT, int LPG, bool ONE>
+__global__ __launch_bounds__(NT) void k_ste_update(SteK<WT> a) {
+  const int64_t gid = ((int64_t)blockIdx.x * NT + threadIdx.x) / LPG;
+  const int lig = threadIdx.x % LPG;
+  if (gid >= a.ngroups) return;
+  const Grid gr = grid_of(a.gr);
+  const int64_t n = gid / a.Gn;
+  const int64_t base = n * a.K + (gid - n * a.Gn) * a.g;
+  const int E = ONE ? 1 : a.E;
+  const int64_t off0 = base + 8 * lig;
+
+  // phase 1: group min / max (the Min-Max range)
+  float w0[8], v0[8], g0[8];
+  float mn = INFINITY, mx = -INFINITY;
+  for (int e = 0; e < E; ++e) {
+    float w[8];
+    load8(a.W + off0 + 8 * LPG * e, w);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      mn = fminf(mn, w[i]);
+      mx = fmaxf(mx, w[i]);
+      if (ONE) w0[i] = w[i];
+    }
+  }
+  mn = group_min<LPG>(mn);
+  mx = group_max<LPG>(mx);
+  const float al = a.alpha[gid], be = a.beta[gid];
+  const QP p = group_qparams(mn, mx, al, be, gr);
+
+  // phase 2: straight-through sums over the group
+  float A = 0.0f, Bs = 0.0f;
+  if (ONE) {
+    load8(a.V + off0, v0);
+    load8(a.G + off0, g0);
+    ste_accum(w0, v0, g0, p, gr, A, Bs);
+  } else {
+    for (int e = 0; e < E; ++e) {
+      float w[8], v[8], g[8];
+      const int64_t off = off0 + 8 * LPG * e;
+      load8(a.W + off, w);
+      load8(a.V + off, v);
+      load8(a.G + off, g);
+      ste_accum(w, v, g, p, gr, A, Bs);
+    }
+  }
+  A = group_sum<LPG>(A);
+  Bs = group_sum<LPG>(Bs);
+
+  // clip-factor gradients (zero for a zero-range group)
+  float ga = 0.0f, gb = 0.0f;
+  if (!p.zero) {
+    if (gr.sym) {
+      const float damax = 2.0f * A / gr.maxq;
+      const bool to_alpha = fabsf(al * mn) > fabsf(be * mx);
+      ga = to_alpha ? damax * fabsf(mn) : 0.0f;
+      gb = to_alpha ? 0.0f : damax * fabsf(mx);
+    } else {
+      const float B = -p.s * Bs;
+      const float D = A + B * p.lo / (p.s * p.s);
+      const float dlo = -D / gr.maxq - B / p.s;
+      const float dhi = D / gr.maxq;
+      ga = (mn < 0.0f) ? dlo * mn : 0.0f;
+      gb = (mx > 0.0f) ? dhi * mx : 0.0f;
+    }
+  }
+  const bool snap = a.flag != nullptr && *a.flag != 0;
+  float an = al, bn = be;
+  if (a.apply) {
+    an = fminf(fmaxf(al - a.mlr * sgnf(ga), a.clip_lo), a.clip_hi);
+    bn = fminf(fmaxf(be - a.mlr * sgnf(gb), a.clip_lo), a.clip_hi);
+  }
+  if (lig == 0) {
+    if (a.gA) a.gA[gid] = ga;
+    if (a.gB) a.gB[gid] = gb;
+    if (snap) { a.bestA[gid] = al; a.bestB[gid] = be; }
+    if (a.apply) { a.alpha[gid] = an; a.beta[gid] = bn; }
+  }
+  const QP pn = group_qparams(mn, mx, an, bn, gr);
+
+  // phase 3: offsets, snapshot, next fake-quant
+  if (ONE) {
+    ste_finish(a, off0, w0, v0, g0, p, pn, gr, snap);
+  } else {
+    for (int e = 0; e < E; ++e) {
+      float w[8], v[8], g[8];
+      const int64_t off = off0 + 8 * LPG * e;
+      load8(a.W + off, w);
+      load8(a.V + off, v);
+      load8(a.G + off, g);
+      ste_finish(a, off, w, v, g, p, pn, gr, snap);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ loss
+// loss = (sum of per-tile sums of R²) / (Tb·N), summed in a fixed order in
+// float64; strict "<" against the best loss decides the snapshot.
+__global__ __launch_bounds__(NT) void k_loss_finalize(const float* partials, int nparts,
+                                                      double inv_count, float* loss_out,
+                                                      float* loss_slot, float* best_loss,
+                                                      int* flag) {
+  __shared__ double sh[NT];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < nparts; i += NT) acc += (double)partials[i];
+  sh[threadIdx.x] = acc;
+  __syncthreads();
+  for (int s = NT / 2; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float L = (float)(sh[0] * inv_count);
+    if (loss_out) *loss_out = L;
+    if (loss_slot) *loss_slot = L;
+    int imp = 0;
+    if (best_loss) {
+      imp = L < *best_loss;
+      if (imp) *best_loss = L;
+    }
+    *flag = imp;
+  }
+}
+
+// ------------------------------------------------------------------ transpose
+template <typename T>
+__global__ __launch_bounds__(NT) void k_transpose(const T* __restrict__ src, T* __restrict__ dst,
+                                                  int64_t R, int64_t C) {
+  __shared__ T tile[64][65];
+  const int64_t b = blockIdx.z;
+  src += b * R * C;
+  dst += b * R * C;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    if (r < R && c < C) tile[i][tx] = src[r * C + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < C && r < R) dst[c * R + r] = tile[tx][i];
+  }
+}
+
+__global__ __launch_bounds__(NT) void k_fill_f32(float* p, float v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT)
+    p[i] = v;
+}
+
+// ------------------------------------------------------------------ packing
+// A block of CB codes (CB*BITS bits) fills WB whole words: 3-bit codes go 32
+// per 3 words; 2/4/8-bit codes 16/8/4 per word.
+template <int BITS>
+struct PackShape {
+  static constexpr int WB = (BITS == 3) ? 3 : 1;
+  static constexpr int CB = 32 * WB / BITS;
+  static constexpr uint32_t MASK = (1u << BITS) - 1u;
+};
+
+template <int BITS>
+__device__ __forceinline__ void put_code(uint32_t* out, int c, uint32_t code) {
+  const int pos = c * BITS, w = pos >> 5, off = pos & 31;
+  out[w] |= code << off;
+  if (off + BITS > 32) out[w + 1] |= code >> (32 - off);
+}
+template <int BITS>
+__device__ __forceinline__ uint32_t get_code(const uint32_t* in, int c) {
+  const int pos = c * BITS, w = pos >> 5, off = pos & 31;
+  uint32_t v = in[w] >> off;
+  if (off + BITS > 32) v |= in[w + 1] << (32 - off);
+  return v & PackShape<BITS>::MASK;
+}
+
+// codes [N, K] -> qweight [K*BITS/32, N]. A workgroup stages a 64 x 256 code
+// tile in LDS (coalesced row reads), then each thread packs one block of one
+// row and the stores of consecutive threads hit consecutive columns.
+template <int BITS>
+__global__ __launch_bounds__(NT) void k_pack_w(const uint8_t* __restrict__ codes,
+                                               uint32_t* __restrict__ qw, int64_t N, int64_t K) {
+  using S = PackShape<BITS>;
+  __shared__ uint32_t tile[64][65];
+  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 256;
+  for (int i = threadIdx.x; i < 64 * 64; i += NT) {
+    const int r = i >> 6, c = i & 63;
+    const int64_t n = n0 + r, k = k0 + 4 * c;
+    uint32_t v = 0;
+    if (n < N && k < K) v = *reinterpret_cast<const uint32_t*>(codes + n * K + k);
+    tile[r][c] = v;
+  }
+  __syncthreads();
+  constexpr int NB = 256 / S::CB;
+  const int64_t wrow0 = k0 * BITS / 32;
+  for (int it = threadIdx.x; it < 64 * NB; it += NT) {
+    const int r = it & 63, blk = it >> 6;
+    const int64_t n = n0 + r, kb = k0 + (int64_t)blk * S::CB;
+    if (n >= N || kb >= K) continue;
+    uint32_t out[S::WB + 1] = {};
+    for (int c = 0; c < S::CB; ++c) {
+      const int byte = blk * S::CB + c;
+      put_code<BITS>(out, c, (tile[r][byte >> 2] >> (8 * (byte & 3))) & S::MASK);
+    }
+#pragma unroll
+    for (int w = 0; w < S::WB; ++w) qw[(wrow0 + (int64_t)blk * S::WB + w) * N + n] = out[w];
+  }
+}
+
+// zp [N, G] -> qzeros [G, N*BITS/32]: same bit layout along N.
+template <int BITS>
+__global__ __launch_bounds__(NT) void k_pack_z(const uint8_t* __restrict__ zp,
+                                               uint32_t* __restrict__ qz, int64_t N, int64_t G) {
+  using S = PackShape<BITS>;
+  const int64_t nblk = N / S::CB;
+  const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (idx >= G * nblk) return;
+  const int64_t j = idx / nblk, blk = idx - j * nblk;
+  uint32_t out[S::WB + 1] = {};
+  for (int c = 0; c < S::CB; ++c) put_code<BITS>(out, c, zp[(blk * S::CB + c) * G + j] & S::MASK);
+  const int64_t words = N * BITS / 32;
+#pragma unroll
+  for (int w = 0; w < S::WB; ++w) qz[j * words + blk * S::WB + w] = out[w];
+}
+
+template <int BITS>
+__global__ __launch_bounds__(NT) void k_unpack_w(const uint32_t* __restrict__ qw,
+                                                 uint8_t* __restrict__ codes, int64_t N, int64_t K) {
+  using S = PackShape<BITS>;
+  const int64_t nblk = K / S::CB;
+  const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (idx >= N * nblk) return;
+  const int64_t blk = idx / N, n = idx - blk * N;
+  uint32_t in[S::WB + 1] = {};
+#pragma unroll
+  for (int w = 0; w < S::WB; ++w) in[w] = qw[(blk * S::WB + w) * N + n];
+  for (int c = 0; c < S::CB; ++c) codes[n * K + blk * S::CB + c] = (uint8_t)get_code<BITS>(in, c);
+}
+
+template <int BITS>
+__global__ __launch_bounds__(NT) void k_unpack_z(const uint32_t* __restrict__ qz,
+                                                 uint8_t* __restrict__ zp, int64_t N, int64_t G) {
+  using S = PackShape<BITS>;
+  const int64_t nblk = N / S::CB;
+  const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (idx >= G * nblk) return;
+  const int64_t j = idx / nblk, blk = idx - j * nblk;
+  const int64_t words = N * BITS / 32;
+  uint32_t in[S::WB + 1] = {};
+#pragma unroll
+  for (int w = 0; w < S::WB; ++w) in[w] = qz[j * words + blk * S::WB + w];
+  for (int c = 0; c < S::CB; ++c) zp[(blk * S::CB + c) * G + j] = (uint8_t)get_code<BITS>(in, c);
+}
+
+inline unsigned blocks_for(int64_t threads) { return (unsigned)((threads + NT - 1) / NT); }
+inline ar_status last_status() { return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP; }
+
+template <typename WT, typename OT>
+ar_status fq_dispatch(FQArgs<WT, OT> a, int lpg, hipStream_t st) {
+  const unsigned nb = blocks_for(a.ngroups * lpg);
+  switch (lpg) {
+#define AR_FQ_CASE(L) \
+  case L: hipLaunchKernelGGL((k_fakequant<WT, OT, L>), dim3(nb), dim3(NT), 0, st, a); break;
+    AR_FQ_CASE(1) AR_FQ_CASE(2) AR_FQ_CASE(4) AR_FQ_CASE(8) AR_FQ_CASE(16) AR_FQ_CASE(32)
+    AR_FQ_CASE(64)
+#undef AR_FQ_CASE
+    default: return AR_ERR_INVALID_ARG;
+  }
+  return last_status();
+}
+
+template <typename WT, typename OT>
+ar_status fq_make(const void* W, const float* V, const float* alpha, const float* beta,
+                  float shrink, int64_t N, int64_t K, int g, ArGrid gr, void* Wq, uint8_t* codes,
+                  float* scale, uint8_t* zp, hipStream_t st) {
+  int lpg, E;
+  ar_group_layout(g, &lpg, &E);
+  FQArgs<WT, OT> a{static_cast<const WT*>(W), V, alpha, beta, shrink, N * (K / g), K, g,
+                   (int)(K / g), E, gr, static_cast<OT*>(Wq), codes, scale, zp};
+  return fq_dispatch(a, lpg, st);
+}
+
+template <typename WT>
+ar_status ste_make(const ArSteArgs& s, hipStream_t st) {
+  int lpg, E;
+  ar_group_layout(s.g, &lpg, &E);
+  SteK<WT> a{static_cast<const WT*>(s.W), s.V, s.alpha, s.beta, s.G, s.N * (s.K / s.g), s.K,
+             s.g, (int)(s.K / s.g), E, s.gr, s.lr, s.mlr, s.clip_lo, s.clip_hi, s.flag,
+             s.bestV, s.bestA, s.bestB, s.gV, s.gA, s.gB, s.apply, s.Wq_next};
+  const unsigned nb = blocks_for(a.ngroups * lpg);
+  switch (lpg * 2 + (E == 1 ? 1 : 0)) {
+#define AR_STE_CASE(L)                                                                          \
+  case 2 * L + 1:                                                                               \
+    hipLaunchKernelGGL((k_ste_update<WT, L, true>), dim3(nb), dim3(NT), 0, st, a); break;       \
+  case 2 * L:                                                                                   \
+    hipLaunchKernelGGL((k_ste_update<WT, L, false>), dim3(nb), dim3(NT), 0, st, a); break;
+    AR_STE_CASE(1) AR_STE_CASE(2) AR_STE_CASE(4) AR_STE_CASE(8) AR_STE_CASE(16)
+    AR_STE_CASE(32) AR_STE_CASE(64)
+#undef AR_STE_CASE
+    default: return AR_ERR_INVALID_ARG;
+  }
+  return last_status();
+}
+
+}  // namespace
+
+ar_status ar_launch_fakequant(int wdt, const void* W, const float* V, const float* alpha,
+                              const float* beta, float shrink, int64_t N, int64_t K, int g,
+                              ArGrid gr, int out_dt, void* Wq, uint8_t* codes, float* scale,
+                              uint8_t* zp, hipStream_t st) {
+  if (wdt == AR_BF16) {
+    if (out_dt == AR_BF16)
+      return fq_make<uint16_t, uint16_t>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, codes, scale, zp, st);
+    return fq_make<uint16_t, float>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, codes, scale, zp, st);
+  }
+  if (out_dt == AR_BF16)
+    return fq_make<float, uint16_t>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, codes, scale, zp, st);
+  return fq_make<float, float>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, codes, scale, zp, st);
+}
+
+ar_status ar_launch_ste_update(const ArSteArgs& s, hipStream_t st) {
+  return s.wdt == AR_BF16 ? ste_make<uint16_t>(s, st) : ste_make<float>(s, st);
+}
+
+ar_status ar_launch_loss_finalize(const float* partials, int nparts, double inv_count,
+                                  float* loss_out, float* loss_slot, float* best_loss, int* flag,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL(k_loss_finalize, dim3(1), dim3(NT), 0, st, partials, nparts, inv_count,
+                     loss_out, loss_slot, best_loss, flag);
+  return last_status();
+}
+
+ar_status ar_launch_transpose(const void* src, void* dst, int64_t batch, int64_t R, int64_t C,
+                              int elem_bytes, hipStream_t st) {
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64), (unsigned)batch);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(NT), 0, st,
+                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C);
+  else
+    hipLaunchKernelGGL(k_transpose<uint32_t>, grid, dim3(NT), 0, st,
+                       static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), R, C);
+  return last_status();
+}
+
+ar_status ar_launch_fill_f32(float* p, float v, int64_t n, hipStream_t st) {
+  if (n <= 0) return AR_OK;
+  const int64_t want = (n + NT - 1) / NT;
+  const unsigned nb = (unsigned)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(k_fill_f32, dim3(nb), dim3(NT), 0, st, p, v, n);
+  return last_status();
+}
+
+ar_status ar_launch_pack(int bits, const uint8_t* codes, const uint8_t* zp, int64_t N, int64_t K,
+                         int64_t G, int32_t* qweight, int32_t* qzeros, hipStream_t st) {
+  const dim3 gw((unsigned)((K + 255) / 256), (unsigned)((N + 63) / 64));
+  uint32_t* qw = reinterpret_cast<uint32_t*>(qweight);
+  uint32_t* qz = reinterpret_cast<uint32_t*>(qzeros);
+  switch (bits) {
+#define AR_PACK_CASE(B)                                                                       \
+  case B:                                                                                     \
+    hipLaunchKernelGGL(k_pack_w<B>, gw, dim3(NT), 0, st, codes, qw, N, K);                    \
+    if (zp)                                                                                   \
+      hipLaunchKernelGGL(k_pack_z<B>, dim3(blocks_for(G * (N / PackShape<B>::CB))), dim3(NT), \
+                         0, st, zp, qz, N, G);                                                \
+    break;
+    AR_PACK_CASE(2) AR_PACK_CASE(3) AR_PACK_CASE(4) AR_PACK_CASE(8)
+#undef AR_PACK_CASE
+    default: return AR_ERR_UNSUPPORTED;
+  }
+  return last_status();
+}
+
+ar_status ar_launch_unpack(int bits, const int32_t* qweight, const int32_t* qzeros, int64_t N,
+                           int64_t K, int64_t G, uint8_t* codes, uint8_t* zp, hipStream_t st) {
+  const uint32_t* qw = reinterpret_cast<const uint32_t*>(qweight);
+  const uint32_t* qz = reinterpret_cast<const uint32_t*>(qzeros);
+  switch (bits) {
+#define AR_UNPACK_CASE(B)                                                                       \
+  case B:                                                                                       \
+    hipLaunchKernelGGL(k_unpack_w<B>, dim3(blocks_for(N * (K / PackShape<B>::CB))), dim3(NT),   \
+                       0, st, qw, codes, N, K);                                                 \
+    if (zp)                                                                                     \
+      hipLaunchKernelGGL(k_unpack_z<B>, dim3(blocks_for(G * (N / PackShape<B>::CB))), dim3(NT), \
+                         0, st, qz, zp, N, G);                                                  \
+    break;
+    AR_UNPACK_CASE(2) AR_UNPACK_CASE(3) AR_UNPACK_CASE(4) AR_UNPACK_CASE(8)
+#undef AR_UNPACK_CASE
+    default: return AR_ERR_UNSUPPORTED;
+  }
+  return last_status();
+}

@@ -1,0 +1,192 @@
+/*
+ * autoround_hip.h - C ABI of the MI355X (gfx950) AutoRound per-Linear tuning library.
+ *
+ * AutoRound tunes, per weight group, a rounding offset V in [-0.5, 0.5] and two
+ * clip factors (alpha on the group minimum, beta on the group maximum) by
+ * SignSGD so that the fake-quantized weight Ŵ = s*(clamp(rint(W/s + V) + zp) - zp)
+ * reproduces the layer output X·Wᵀ on calibration tokens; the final integer codes
+ * are then packed into 32-bit words.
+ *
+ * Sources (page title, section):
+ *   [LLMC]  "[llm-compressor] AutoRound: 부호 경사 하강법으로 라운딩 최적화":
+ *           paper-core equations (RTN, learnable offset, SignSGD), constructor
+ *           parameter table, the per-module tuning loop, _fake_quantize_with_offset.
+ *   [INTEL] "Introducing AutoRound: Intel's Advanced Quantization for LLMs and VLMs":
+ *           section 2 (rounding and clipping range tuned jointly), section 4
+ *           (zero iterations = RTN; 8/4/3/2-bit).
+ *   [SGL]   "[SGLang] AutoRound: 자동 라운딩 최적화 양자화": "1. AutoRoundConfig"
+ *           (bits {2,3,4,8}, sym, pack_factor = Fraction(32, bits)), "설계 근거"
+ *           (GPTQ/AWQ packing reuse).
+ *
+ * Conventions for every entry point:
+ *   - Every array pointer is a caller-owned DEVICE pointer (hipMalloc / torch),
+ *     row-major and contiguous, 16-byte aligned. The library never allocates
+ *     device memory; scratch space comes in through (ws, ws_bytes).
+ *   - `stream` is a hipStream_t (NULL = default stream). All device work is
+ *     enqueued asynchronously on it, except where an entry point says it blocks.
+ *   - Arguments are validated before anything is enqueued; on any error status
+ *     nothing has been written. No C++ exception crosses this interface.
+ *   - Shapes: W is [N, K] (N out features, K in features, torch Linear layout).
+ *     K must be a multiple of 8 and of group_size; G = K / group_size groups per
+ *     row (group_size = -1: one group of K per row). group_size must be a
+ *     multiple of 8. N >= 1 and K >= 8, except where an entry point accepts N*K = 0.
+ *   - bf16 data is passed as uint16 bit patterns.
+ */
+#ifndef AUTOROUND_HIP_H
+#define AUTOROUND_HIP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AR_OK = 0,
+  AR_ERR_INVALID_ARG = 1,   /* null pointer, bad hyper-parameter, misaligned pointer */
+  AR_ERR_UNSUPPORTED = 2,   /* bits not in {2,3,4,8} (16 = "leave unquantized"), bad dtype */
+  AR_ERR_SHAPE = 3,         /* size constraint violated */
+  AR_ERR_WORKSPACE = 4,     /* ws_bytes smaller than the *_workspace_size result */
+  AR_ERR_HIP = 6            /* a HIP runtime call or kernel launch failed */
+} ar_status;
+
+typedef enum { AR_F32 = 0, AR_BF16 = 1 } ar_dtype;
+
+/* Tuning hyper-parameters; names as on the [LLMC] constructor parameter table. */
+typedef struct {
+  int32_t bits;          /* {2,3,4,8}: [SGL] 1. AutoRoundConfig SUPPORTED_BITS            */
+  int32_t group_size;    /* input channels per group; -1 = whole row                      */
+  int32_t sym;           /* 0: asymmetric (zero-point from the range), 1: symmetric        */
+  int32_t nsamples;      /* calibration samples ([LLMC] default 128)                       */
+  int32_t seqlen;        /* tokens per sample ([LLMC] default 2048)                        */
+  int32_t batch_samples; /* samples per SignSGD step; nsamples % batch_samples == 0        */
+  int32_t iters;         /* SignSGD steps ([LLMC] default 200); 0 = RTN ([INTEL] sec. 4)   */
+  float lr;              /* offset step ([LLMC] default 0.005)                             */
+  float minmax_lr;       /* clip-factor step; < 0 means "unset" = lr ([LLMC] minmax_lr)    */
+  float minmax_shrink;   /* initial alpha = beta ([LLMC] minmax_shrink, default 1.0)       */
+  float clip_lo;         /* alpha/beta lower clamp (default 0.5)                           */
+  float clip_hi;         /* alpha/beta upper clamp (default 1.0)                           */
+} ar_config;
+
+/* Per-kernel device time of one ar_tune_linear call (milliseconds, summed over
+   launches), measured with HIP events recorded on the call's stream. */
+typedef struct {
+  double fwd_gemm_ms;    /* Y' = X_b·Ŵᵀ with residual / loss / dY epilogue */
+  double wgrad_gemm_ms;  /* G = (2/(T_b·N))·dYᵀ·X_b                         */
+  double ste_update_ms;  /* straight-through fold + SignSGD + next fake-quant */
+  double loss_ms;        /* loss reduction + best-loss decision              */
+  int64_t steps;         /* number of SignSGD steps timed                    */
+} ar_kernel_times;
+
+/* Fill *cfg with the [LLMC] defaults: bits 4, group_size 128, asym, nsamples 128,
+   seqlen 2048, batch_samples 8, iters 200, lr 0.005, minmax_lr unset (-1),
+   minmax_shrink 1.0, clip range [0.5, 1.0]. Returns AR_ERR_INVALID_ARG on NULL. */
+ar_status ar_config_default(ar_config* cfg);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* ar_status_string(int32_t status);
+
+/* Bytes of device workspace ar_tune_linear needs for this problem (X is
+   [nsamples*seqlen, K] bf16, Y is [nsamples*seqlen, N] of dtype ydt). */
+ar_status ar_workspace_size(const ar_config* cfg, int64_t N, int64_t K, int32_t ydt,
+                            size_t* bytes);
+
+/* Bytes of device workspace ar_tune_step needs for a minibatch of Tb tokens. */
+ar_status ar_step_workspace_size(const ar_config* cfg, int64_t N, int64_t K, int64_t Tb,
+                                 int32_t ydt, size_t* bytes);
+
+/* Round-to-nearest quantization ([LLMC] paper-core RTN equation): V = 0 and
+   alpha = beta = cfg->minmax_shrink; group min/max from W ([LLMC] tuning loop,
+   Min-Max initial scale).
+   W      [N, K] of dtype wdt (AR_F32 or AR_BF16)
+   codes  [N, K] uint8 in [0, 2^bits-1]        (nullable)
+   scale  [N, G] float32                       (nullable)
+   zp     [N, G] uint8 zero-points              (nullable)
+   Wq     [N, K] of dtype wdt, s*(code - zp)    (nullable)
+   N*K = 0 is a no-op. */
+ar_status ar_rtn_quant(const ar_config* cfg, int32_t wdt, const void* W, int64_t N, int64_t K,
+                       uint8_t* codes, float* scale, uint8_t* zp, void* Wq, void* stream);
+
+/* Fake-quantization with learnable offset and clip factors ([LLMC] paper-core
+   offset equation and _fake_quantize_with_offset; [INTEL] sec. 2 clip range):
+   per group lo = min(alpha*wmin, 0), hi = max(beta*wmax, 0), s = (hi-lo)/maxq,
+   zp = clamp(rint(-lo/s), 0, maxq)  (sym: s = 2*max(|alpha*wmin|, |beta*wmax|)/maxq,
+   zp = 2^(bits-1)); per element code = clamp(rint(W/s + V) + zp, 0, maxq),
+   Ŵ = s*(code - zp). A zero-range group uses s = 1. All float32, rint = half-even.
+   V [N, K] float32; alpha, beta [N, G] float32.
+   Wq_bf16 [N, K] bf16 Ŵ (nullable); codes, scale, zp as in ar_rtn_quant (nullable).
+   N*K = 0 is a no-op. */
+ar_status ar_fakequant_fwd(const ar_config* cfg, int32_t wdt, const void* W, int64_t N,
+                           int64_t K, const float* V, const float* alpha, const float* beta,
+                           uint16_t* Wq_bf16, uint8_t* codes, float* scale, uint8_t* zp,
+                           void* stream);
+
+/* Tuning state of one Linear, all device pointers owned by the caller. */
+typedef struct {
+  const void* W;       /* [N, K] weight, dtype wdt          */
+  int32_t wdt;         /* AR_F32 or AR_BF16                  */
+  int64_t N, K;
+  float* V;            /* [N, K] offsets, updated in place   */
+  float* alpha;        /* [N, G] min clip factors, in place  */
+  float* beta;         /* [N, G] max clip factors, in place  */
+  float* best_V;       /* [N, K] best-state snapshot   (nullable: no snapshot; the four
+                          best_* pointers are all set or all NULL) */
+  float* best_alpha;   /* [N, G]                              */
+  float* best_beta;    /* [N, G]                              */
+  float* best_loss;    /* device scalar; caller initialises it to +inf */
+} ar_state;
+
+/* One SignSGD iteration on one minibatch ([LLMC] tuning loop; [LLMC] SignSGD
+   equation). From the current state: Ŵ (bf16 operand), Y' = Xb·Ŵᵀ (bf16 MFMA,
+   float32 accumulation), R = Y' - Yb, loss = sum(R²)/(Tb·N) -> loss_out[0];
+   dY = bf16(R); G = (2/(Tb·N))·dYᵀ·Xb; straight-through fold to dL/dV, dL/dalpha,
+   dL/dbeta. If best_* are set and loss < *best_loss, the current (pre-update)
+   state is copied to best_* and *best_loss = loss. If apply_update != 0:
+   V <- clamp(V - lr·sgn(dL/dV), -0.5, 0.5), alpha/beta <- clamp(· - minmax_lr·sgn, clip_lo, clip_hi).
+   Xb [Tb, K] bf16; Yb [Tb, N] of dtype ydt; Tb > 0, Tb % 8 == 0.
+   loss_out: device float (required). gV [N, K], galpha/gbeta [N, G] float32:
+   pre-update gradients (nullable). ws: ar_step_workspace_size bytes. */
+ar_status ar_tune_step(const ar_config* cfg, const ar_state* state, const uint16_t* Xb,
+                       const void* Yb, int32_t ydt, int64_t Tb, float* loss_out, float* gV,
+                       float* galpha, float* gbeta, int32_t apply_update, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* The whole per-Linear tuning loop ([LLMC] tuning loop with best-loss snapshot):
+   V = 0, alpha = beta = minmax_shrink; step i uses minibatch b = i mod
+   (nsamples/batch_samples), i.e. rows [b*Tb, (b+1)*Tb) of X and Y with
+   Tb = batch_samples*seqlen; after cfg->iters steps the state with the lowest
+   loss (strictly lower than all before it, evaluated before its update) is
+   restored and quantized. iters = 0 gives RTN ([INTEL] section 4).
+   W [N, K] wdt; X [nsamples*seqlen, K] bf16; Y [nsamples*seqlen, N] ydt.
+   Outputs: codes [N, K] uint8, scale [N, G] float32, zp [N, G] uint8 (required);
+   Wq [N, K] wdt (nullable); V_out [N, K], alpha_out/beta_out [N, G] float32 final
+   (restored) state (nullable); losses [iters] float32 per-step loss (nullable).
+   ws: ar_workspace_size bytes. times: when non-NULL, per-kernel device times are
+   measured with HIP events and the call blocks until the stream has drained. */
+ar_status ar_tune_linear(const ar_config* cfg, int32_t wdt, const void* W, int64_t N, int64_t K,
+                         const uint16_t* X, const void* Y, int32_t ydt, uint8_t* codes,
+                         float* scale, uint8_t* zp, void* Wq, float* V_out, float* alpha_out,
+                         float* beta_out, float* losses, void* ws, size_t ws_bytes,
+                         ar_kernel_times* times, void* stream);
+
+/* Pack codes into 32-bit words ([SGL] pack_factor = Fraction(32, bits); GPTQ-style
+   layout): code (n, k) occupies bits [k*bits, (k+1)*bits) of the bit string of
+   column n, least significant bit first, so word w of column n is
+   qweight[w, n] (a 3-bit code that straddles two words is split, low bits first).
+   codes [N, K] uint8 -> qweight [K*bits/32, N] int32.
+   zp [N, G] uint8 -> qzeros [G, N*bits/32] int32, same scheme along N (zp and
+   qzeros nullable together). Requires K*bits % 32 == 0, and N*bits % 32 == 0
+   when zp is given. N*K = 0 is a no-op. */
+ar_status ar_pack(int32_t bits, const uint8_t* codes, const uint8_t* zp, int64_t N, int64_t K,
+                  int64_t G, int32_t* qweight, int32_t* qzeros, void* stream);
+
+/* Inverse of ar_pack (same shapes and constraints). */
+ar_status ar_unpack(int32_t bits, const int32_t* qweight, const int32_t* qzeros, int64_t N,
+                    int64_t K, int64_t G, uint8_t* codes, uint8_t* zp, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AUTOROUND_HIP_H */

@@ -1,0 +1,66 @@
+"""Write oracle-computed expected values for the long-loop GPU parity test.
+
+Calls only ``oracle`` and ``synth`` (never the HIP library). Runs the full
+200-iteration tuning loop of a named workload on the CPU and stores, for a
+fixed sample of output rows, the final codes / scales / zero-points / clip
+factors, plus the whole loss trajectory and the best step.
+
+    python tests/golden/make_golden.py llama7b_q_proj      # ~15 min on 8 cores
+"""
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import oracle as O  # noqa: E402
+import synth  # noqa: E402
+
+N_ROWS = 128
+ROW_SEED = 123
+
+
+def sample_rows(N):
+    return np.sort(np.random.default_rng(ROW_SEED).choice(N, size=min(N_ROWS, N), replace=False))
+
+
+def main(name):
+    w = synth.WORKLOADS[name]
+    t0 = time.time()
+    case = synth.make_workload_case(w)
+    Y = synth.reference_outputs(case)
+    print(f"inputs ready {time.time() - t0:.1f}s", flush=True)
+    cfg = O.Config(bits=w.bits, group_size=w.group_size, sym=w.sym, nsamples=w.nsamples,
+                   seqlen=w.seqlen, batch_samples=w.batch_samples, iters=w.iters, lr=w.lr,
+                   minmax_lr=w.minmax_lr, minmax_shrink=w.minmax_shrink)
+    Tb = w.Tb
+    nb = w.nsamples // w.batch_samples
+
+    def minibatch(b):
+        xb = synth.bf16_bits_to_f32(case.X_bits[b * Tb:(b + 1) * Tb])
+        yb = Y[b * Tb:(b + 1) * Tb]
+        yb = synth.bf16_bits_to_f32(yb) if w.wdtype == "bf16" else yb
+        return xb, yb
+
+    def on_step(i, r):
+        print(f"step {i} loss {r.loss:.9e} t={time.time() - t0:.0f}s", flush=True)
+
+    res = O.tune_linear(case.W, minibatch, nb, cfg, on_step=on_step)
+    rtn_codes, _, _, _ = O.rtn_quant(case.W, cfg)
+    rows = sample_rows(w.N)
+    out = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"tune_{name}.npz")
+    np.savez_compressed(
+        out, rows=rows, losses=np.array(res.losses, np.float64),
+        best_step=np.int64(res.best_step), best_loss=np.float64(res.best_loss),
+        codes=res.codes[rows], scale=res.scale[rows], zp=res.zp[rows],
+        alpha=res.alpha[rows], beta=res.beta[rows],
+        changed_vs_rtn=np.float64((res.codes != rtn_codes).mean()))
+    print(f"wrote {out}; best step {res.best_step} loss {res.best_loss:.6e}; "
+          f"codes changed vs RTN {(res.codes != rtn_codes).mean():.4f}", flush=True)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1] if len(sys.argv) > 1 else "llama7b_q_proj")
