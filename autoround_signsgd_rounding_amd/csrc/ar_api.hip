@@ -6,6 +6,7 @@
 
 #include <vector>
 
+#include "ar_blocked.h"
 #include "ar_launch.h"
 
 namespace {
@@ -72,22 +73,39 @@ struct Carver {
   }
 };
 
+// Element counts of the blocked GEMM operands (ar_blocked.h) for one minibatch.
+struct BlkSizes {
+  int64_t nkbK, nkbT;        // k-blocks along K and along Tb (Tb padded to whole tiles)
+  int64_t xb, xtb, yb, wb;   // elements of XB, XTB, YB, WB / dyB
+  BlkSizes(int64_t N, int64_t K, int64_t Tb) {
+    nkbK = arblk::k_blocks(K);
+    nkbT = arblk::row_tiles(Tb) * (arblk::ROWS / arblk::KB);
+    xb = arblk::row_tiles(Tb) * nkbK * arblk::BLOCK_ELEMS;
+    xtb = arblk::row_tiles(K) * nkbT * arblk::BLOCK_ELEMS;
+    yb = arblk::row_tiles(N) * nkbT * arblk::BLOCK_ELEMS;
+    wb = arblk::row_tiles(N) * nkbK * arblk::BLOCK_ELEMS;
+  }
+};
+
 struct StepWs {
-  uint16_t* XTb;
-  void* YTb;
-  uint16_t* dyT;
-  uint16_t* Wq;
+  uint16_t* XB;
+  uint16_t* XTB;
+  void* YB;
+  uint16_t* dyB;
+  uint16_t* WB;
   float* G;
   float* partials;
   int* flag;
 };
 StepWs carve_step(void* ws, int64_t N, int64_t K, int64_t Tb, int32_t ydt, size_t* bytes) {
   Carver c{static_cast<uint8_t*>(ws)};
+  const BlkSizes z(N, K, Tb);
   StepWs w;
-  w.XTb = c.take<uint16_t>((size_t)K * Tb * 2);
-  w.YTb = c.take<uint8_t>((size_t)N * Tb * dsize(ydt));
-  w.dyT = c.take<uint16_t>((size_t)N * Tb * 2);
-  w.Wq = c.take<uint16_t>((size_t)N * K * 2);
+  w.XB = c.take<uint16_t>((size_t)z.xb * 2);
+  w.XTB = c.take<uint16_t>((size_t)z.xtb * 2);
+  w.YB = c.take<uint8_t>((size_t)z.yb * dsize(ydt));
+  w.dyB = c.take<uint16_t>((size_t)z.yb * 2);
+  w.WB = c.take<uint16_t>((size_t)z.wb * 2);
   w.G = c.take<float>((size_t)N * K * 4);
   w.partials = c.take<float>((size_t)ar_fwd_tiles(Tb, N) * 4);
   w.flag = c.take<int>(16);
@@ -96,10 +114,11 @@ StepWs carve_step(void* ws, int64_t N, int64_t K, int64_t Tb, int32_t ydt, size_
 }
 
 struct LoopWs {
-  uint16_t* XT;   // [nb][K][Tb]
-  void* YT;       // [nb][N][Tb]
-  uint16_t* dyT;  // [N][Tb]
-  uint16_t* Wq;   // [N][K] bf16 forward operand
+  uint16_t* XB;   // nb minibatches
+  uint16_t* XTB;  // nb minibatches
+  void* YB;       // nb minibatches
+  uint16_t* dyB;
+  uint16_t* WB;   // bf16 forward operand Ŵ
   float* G;
   float *V, *bestV;
   float *alpha, *beta, *bestA, *bestB;
@@ -107,14 +126,16 @@ struct LoopWs {
   float* best_loss;
   int* flag;
 };
-LoopWs carve_loop(void* ws, int64_t N, int64_t K, int64_t M, int64_t Tb, int64_t Gn, int32_t ydt,
+LoopWs carve_loop(void* ws, int64_t N, int64_t K, int64_t nb, int64_t Tb, int64_t Gn, int32_t ydt,
                   size_t* bytes) {
   Carver c{static_cast<uint8_t*>(ws)};
+  const BlkSizes z(N, K, Tb);
   LoopWs w;
-  w.XT = c.take<uint16_t>((size_t)M * K * 2);
-  w.YT = c.take<uint8_t>((size_t)M * N * dsize(ydt));
-  w.dyT = c.take<uint16_t>((size_t)N * Tb * 2);
-  w.Wq = c.take<uint16_t>((size_t)N * K * 2);
+  w.XB = c.take<uint16_t>((size_t)nb * z.xb * 2);
+  w.XTB = c.take<uint16_t>((size_t)nb * z.xtb * 2);
+  w.YB = c.take<uint8_t>((size_t)nb * z.yb * dsize(ydt));
+  w.dyB = c.take<uint16_t>((size_t)z.yb * 2);
+  w.WB = c.take<uint16_t>((size_t)z.wb * 2);
   w.G = c.take<float>((size_t)N * K * 4);
   w.V = c.take<float>((size_t)N * K * 4);
   w.bestV = c.take<float>((size_t)N * K * 4);
@@ -152,32 +173,34 @@ ar_status check_loop_shape(const ar_config* c, int64_t N, int64_t K, int* g, int
 
 // Launches of one SignSGD step once the transposed minibatch is in place.
 ar_status enqueue_step(const ar_config* c, int wdt, const void* W, int64_t N, int64_t K, int g,
-                       const uint16_t* Xb, const uint16_t* XTb, const void* YTb, int32_t ydt,
-                       int64_t Tb, const uint16_t* Wq, uint16_t* dyT, float* G, float* partials,
+                       const uint16_t* XB, const uint16_t* XTB, const void* YB, int32_t ydt,
+                       int64_t Tb, uint16_t* WB, uint16_t* dyB, float* G, float* partials,
                        int* flag, float* loss_out, float* loss_slot, float* best_loss, float* V,
                        float* alpha, float* beta, float* bestV, float* bestA, float* bestB,
-                       float* gV, float* gA, float* gB, int apply, uint16_t* Wq_next,
+                       float* gV, float* gA, float* gB, int apply, bool write_next,
                        hipStream_t st, hipEvent_t* ev /* 8 events or NULL */) {
   const double inv_count = 1.0 / ((double)Tb * (double)N);
   auto rec = [&](int k) {
     return (!ev || hipEventRecord(ev[k], st) == hipSuccess) ? AR_OK : AR_ERR_HIP;
   };
   AR_TRY(rec(0));
-  AR_TRY(ar_launch_gemm_fwd(Xb, Wq, YTb, ydt, dyT, partials, Tb, N, K, st));
+  AR_TRY(ar_launch_gemm_fwd(XB, WB, YB, ydt, dyB, partials, Tb, N, K, st));
   AR_TRY(rec(1));
   AR_TRY(rec(2));
   AR_TRY(ar_launch_loss_finalize(partials, ar_fwd_tiles(Tb, N), inv_count, loss_out, loss_slot,
                                  best_loss, flag, st));
   AR_TRY(rec(3));
   AR_TRY(rec(4));
-  AR_TRY(ar_launch_gemm_wgrad(dyT, XTb, G, N, K, Tb, (float)(2.0 * inv_count), st));
+  AR_TRY(ar_launch_gemm_wgrad(dyB, XTB, G, N, K, Tb, (float)(2.0 * inv_count), st));
   AR_TRY(rec(5));
   ArSteArgs s;
   s.wdt = wdt; s.W = W; s.V = V; s.alpha = alpha; s.beta = beta; s.G = G;
   s.N = N; s.K = K; s.g = g; s.gr = grid_of(c);
   s.lr = c->lr; s.mlr = minmax_lr_of(c); s.clip_lo = c->clip_lo; s.clip_hi = c->clip_hi;
   s.flag = flag; s.bestV = bestV; s.bestA = bestA; s.bestB = bestB;
-  s.gV = gV; s.gA = gA; s.gB = gB; s.apply = apply; s.Wq_next = Wq_next;
+  s.gV = gV; s.gA = gA; s.gB = gB; s.apply = apply;
+  s.Wq_next = write_next ? WB : nullptr;
+  s.wq_nkb = arblk::k_blocks(K);
   AR_TRY(rec(6));
   AR_TRY(ar_launch_ste_update(s, st));
   AR_TRY(rec(7));
@@ -223,7 +246,7 @@ ar_status ar_workspace_size(const ar_config* c, int64_t N, int64_t K, int32_t yd
   if (!bytes) return AR_ERR_INVALID_ARG;
   AR_TRY(check_loop_shape(c, N, K, &g, &M, &Tb));
   if (!dtype_ok(ydt)) return AR_ERR_UNSUPPORTED;
-  carve_loop(nullptr, N, K, M, Tb, K / g, ydt, bytes);
+  carve_loop(nullptr, N, K, M / Tb, Tb, K / g, ydt, bytes);
   return AR_OK;
 }
 
@@ -246,7 +269,7 @@ ar_status ar_rtn_quant(const ar_config* c, int32_t wdt, const void* W, int64_t N
   if (g == 0) return AR_OK;
   if (!W || !a16(W) || !a16(Wq) || !a8(codes)) return AR_ERR_INVALID_ARG;
   return ar_launch_fakequant(wdt, W, nullptr, nullptr, nullptr, c->minmax_shrink, N, K, g,
-                             grid_of(c), wdt, Wq, codes, scale, zp,
+                             grid_of(c), wdt, Wq, 0, codes, scale, zp,
                              static_cast<hipStream_t>(stream));
 }
 
@@ -261,7 +284,7 @@ ar_status ar_fakequant_fwd(const ar_config* c, int32_t wdt, const void* W, int64
   if (!W || !V || !alpha || !beta) return AR_ERR_INVALID_ARG;
   if (!a16(W) || !a16(V) || !a16(Wq_bf16) || !a8(codes)) return AR_ERR_INVALID_ARG;
   return ar_launch_fakequant(wdt, W, V, alpha, beta, c->minmax_shrink, N, K, g, grid_of(c),
-                             AR_BF16, Wq_bf16, codes, scale, zp,
+                             AR_BF16, Wq_bf16, 0, codes, scale, zp,
                              static_cast<hipStream_t>(stream));
 }
 
@@ -288,15 +311,19 @@ ar_status ar_tune_step(const ar_config* c, const ar_state* s, const uint16_t* Xb
   if (ws_bytes < need) return AR_ERR_WORKSPACE;
   StepWs w = carve_step(ws, N, K, Tb, ydt, &need);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const BlkSizes z(N, K, Tb);
 
-  AR_TRY(ar_launch_transpose(Xb, w.XTb, 1, Tb, K, 2, st));
-  AR_TRY(ar_launch_transpose(Yb, w.YTb, 1, Tb, N, (int)dsize(ydt), st));
+  // stage the minibatch into the blocked GEMM layouts, Ŵ of the current state
+  AR_TRY(ar_launch_block_copy(Xb, w.XB, 1, Tb, K, z.nkbK, st));
+  AR_TRY(ar_launch_block_transpose(Xb, w.XTB, 1, Tb, K, z.nkbT, 2, st));
+  AR_TRY(ar_launch_block_transpose(Yb, w.YB, 1, Tb, N, z.nkbT, (int)dsize(ydt), st));
+  AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(w.WB), 0.0f, z.wb / 2, st));
   AR_TRY(ar_launch_fakequant(s->wdt, s->W, s->V, s->alpha, s->beta, c->minmax_shrink, N, K, g,
-                             grid_of(c), AR_BF16, w.Wq, nullptr, nullptr, nullptr, st));
-  return enqueue_step(c, s->wdt, s->W, N, K, g, Xb, w.XTb, w.YTb, ydt, Tb, w.Wq, w.dyT, w.G,
+                             grid_of(c), AR_BF16, w.WB, z.nkbK, nullptr, nullptr, nullptr, st));
+  return enqueue_step(c, s->wdt, s->W, N, K, g, w.XB, w.XTB, w.YB, ydt, Tb, w.WB, w.dyB, w.G,
                       w.partials, w.flag, loss_out, nullptr, s->best_loss, s->V, s->alpha,
                       s->beta, s->best_V, s->best_alpha, s->best_beta, gV, galpha, gbeta,
-                      apply_update != 0, nullptr, st, nullptr);
+                      apply_update != 0, false, st, nullptr);
 }
 
 ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t N, int64_t K,
@@ -314,9 +341,10 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
   const int64_t Gn = K / g;
   const int64_t nb = c->nsamples / c->batch_samples;
   size_t need;
-  carve_loop(nullptr, N, K, M, Tb, Gn, ydt, &need);
+  carve_loop(nullptr, N, K, nb, Tb, Gn, ydt, &need);
   if (ws_bytes < need) return AR_ERR_WORKSPACE;
-  LoopWs w = carve_loop(ws, N, K, M, Tb, Gn, ydt, &need);
+  LoopWs w = carve_loop(ws, N, K, nb, Tb, Gn, ydt, &need);
+  const BlkSizes z(N, K, Tb);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t ysz = dsize(ydt);
 
@@ -342,9 +370,11 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
     if (_s != AR_OK) return cleanup(_s); \
   } while (0)
 
-  // one-time staging: minibatch-major transposed copies of X and Y
-  AR_TRY_C(ar_launch_transpose(X, w.XT, nb, Tb, K, 2, st));
-  AR_TRY_C(ar_launch_transpose(Y, w.YT, nb, Tb, N, (int)ysz, st));
+  // one-time staging of every minibatch into the blocked GEMM layouts
+  AR_TRY_C(ar_launch_block_copy(X, w.XB, nb, Tb, K, z.nkbK, st));
+  AR_TRY_C(ar_launch_block_transpose(X, w.XTB, nb, Tb, K, z.nkbT, 2, st));
+  AR_TRY_C(ar_launch_block_transpose(Y, w.YB, nb, Tb, N, z.nkbT, (int)ysz, st));
+  AR_TRY_C(ar_launch_fill_f32(reinterpret_cast<float*>(w.WB), 0.0f, z.wb / 2, st));
   // initial state: V = 0, alpha = beta = minmax_shrink, best = initial, best loss = +inf
   AR_TRY_C(ar_launch_fill_f32(w.V, 0.0f, N * K, st));
   AR_TRY_C(ar_launch_fill_f32(w.bestV, 0.0f, N * K, st));
@@ -356,19 +386,19 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
   const ArGrid gr = grid_of(c);
   if (c->iters > 0)
     AR_TRY_C(ar_launch_fakequant(wdt, W, w.V, w.alpha, w.beta, c->minmax_shrink, N, K, g, gr,
-                                 AR_BF16, w.Wq, nullptr, nullptr, nullptr, st));
+                                 AR_BF16, w.WB, z.nkbK, nullptr, nullptr, nullptr, st));
   for (int i = 0; i < c->iters; ++i) {
     const int64_t b = i % nb;
     AR_TRY_C(enqueue_step(
-        c, wdt, W, N, K, g, X + b * Tb * K, w.XT + b * K * Tb,
-        static_cast<const uint8_t*>(w.YT) + (size_t)b * N * Tb * ysz, ydt, Tb, w.Wq, w.dyT, w.G,
+        c, wdt, W, N, K, g, w.XB + b * z.xb, w.XTB + b * z.xtb,
+        static_cast<const uint8_t*>(w.YB) + (size_t)b * z.yb * ysz, ydt, Tb, w.WB, w.dyB, w.G,
         w.partials, w.flag, nullptr, losses ? losses + i : nullptr, w.best_loss, w.V, w.alpha,
-        w.beta, w.bestV, w.bestA, w.bestB, nullptr, nullptr, nullptr, 1, w.Wq, st,
+        w.beta, w.bestV, w.bestA, w.bestB, nullptr, nullptr, nullptr, 1, true, st,
         ev.empty() ? nullptr : &ev[(size_t)i * 8]));
   }
   // restore the best state and quantize it (the initial state when iters = 0)
   AR_TRY_C(ar_launch_fakequant(wdt, W, w.bestV, w.bestA, w.bestB, c->minmax_shrink, N, K, g, gr,
-                               wdt, Wq, codes, scale, zp, st));
+                               wdt, Wq, 0, codes, scale, zp, st));
   if (V_out && hipMemcpyAsync(V_out, w.bestV, (size_t)N * K * 4, hipMemcpyDeviceToDevice, st))
     return cleanup(AR_ERR_HIP);
   if (alpha_out &&

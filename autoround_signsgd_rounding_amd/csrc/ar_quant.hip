@@ -1,6 +1,6 @@
 // Quantizer-side kernels of the tuning step (gfx950): fake-quant, the
-// straight-through fold + SignSGD update, loss finalisation, transposes and
-// int32 packing. All HBM-bound; every group of g contiguous input channels of
+// straight-through fold + SignSGD update, loss finalisation, staging of the
+// GEMM operands into their blocked layout, and int32 packing. All HBM-bound; every group of g contiguous input channels of
 // one output row is handled by LPG consecutive lanes, each lane streaming
 // 8-element chunks (16 B of bf16 / 32 B of float32) so that a wave reads
 // contiguous, coalesced spans.
@@ -11,6 +11,7 @@
 // the rounding), SGLang AutoRound page "1. AutoRoundConfig" (pack_factor).
 #include <math.h>
 
+#include "ar_blocked.h"
 #include "ar_device.h"
 #include "ar_launch.h"
 
@@ -40,6 +41,7 @@ struct FQArgs {
   int g, Gn, E;
   ArGrid gr;
   OT* Wq;
+  int64_t wq_nkb;   // > 0: Wq in the blocked GEMM layout with this many k-blocks
   uint8_t* codes;
   float* scale;
   uint8_t* zp;
@@ -86,7 +88,12 @@ __global__ __launch_bounds__(NT) void k_fakequant(FQArgs<WT, OT> a) {
       q[i] = qe.q;
       wh[i] = qe.what;
     }
-    if (a.Wq) store8(a.Wq + off, wh);
+    if (a.Wq) {
+      if (a.wq_nkb > 0)
+        store8(a.Wq + arblk::chunk_offset(n, off - n * a.K, a.wq_nkb), wh);
+      else
+        store8(a.Wq + off, wh);
+    }
     if (a.codes) store8_u8(a.codes + off, q);
   }
 }
@@ -111,7 +118,8 @@ struct SteK {
   float* gA;
   float* gB;
   int apply;
-  uint16_t* Wq_next;
+  uint16_t* Wq_next;   // blocked GEMM layout (wq_nkb k-blocks)
+  int64_t wq_nkb;
 };
 
 // Straight-through sums of one chunk: A += G·((q - zp) - m·t), Bs += G·[not m].
@@ -131,7 +139,7 @@ __device__ __forceinline__ void ste_accum(const float (&w)[8], const float (&v)[
 // the pre-update offset, V <- clamp(V - lr·sgn(dL/dV), -0.5, 0.5), and the bf16
 // fake-quant of the updated state for the next forward product.
 template <typename WT>
-__device__ __forceinline__ void ste_finish(const SteK<WT>& a, int64_t off, const float (&w)[8],
+__device__ __forceinline__ void ste_finish(const SteK<WT>& a, int64_t n, int64_t off, const float (&w)[8],
                                            const float (&v)[8], const float (&g)[8], const QP& p,
                                            const QP& pn, const Grid& gr, bool snap) {
   float gv[8], vn[8], wq[8];
@@ -146,7 +154,7 @@ __device__ __forceinline__ void ste_finish(const SteK<WT>& a, int64_t off, const
   if (a.gV) store8(a.gV + off, gv);
   if (snap) store8(a.bestV + off, v);
   if (a.apply) store8(a.V + off, vn);
-  if (a.Wq_next) store8(a.Wq_next + off, wq);
+  if (a.Wq_next) store8(a.Wq_next + arblk::chunk_offset(n, off - n * a.K, a.wq_nkb), wq);
 }
 
 // ONE: each lane holds exactly one chunk of its group (kept in registers
@@ -232,7 +240,7 @@ __global__ __launch_bounds__(NT) void k_ste_update(SteK<WT> a) {
 
   // phase 3: offsets, snapshot, next fake-quant
   if (ONE) {
-    ste_finish(a, off0, w0, v0, g0, p, pn, gr, snap);
+    ste_finish(a, n, off0, w0, v0, g0, p, pn, gr, snap);
   } else {
     for (int e = 0; e < E; ++e) {
       float w[8], v[8], g[8];
@@ -240,7 +248,7 @@ __global__ __launch_bounds__(NT) void k_ste_update(SteK<WT> a) {
       load8(a.W + off, w);
       load8(a.V + off, v);
       load8(a.G + off, g);
-      ste_finish(a, off, w, v, g, p, pn, gr, snap);
+      ste_finish(a, n, off, w, v, g, p, pn, gr, snap);
     }
   }
 }
@@ -274,30 +282,64 @@ __global__ __launch_bounds__(NT) void k_loss_finalize(const float* partials, int
   }
 }
 
-// ------------------------------------------------------------------ transpose
-template <typename T>
-__global__ __launch_bounds__(NT) void k_transpose(const T* __restrict__ src, T* __restrict__ dst,
-                                                  int64_t R, int64_t C) {
-  __shared__ T tile[64][65];
-  const int64_t b = blockIdx.z;
-  src += b * R * C;
-  dst += b * R * C;
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    if (r < R && c < C) tile[i][tx] = src[r * C + c];
-  }
-  __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < C && r < R) dst[c * R + r] = tile[tx][i];
-  }
-}
-
 __global__ __launch_bounds__(NT) void k_fill_f32(float* p, float v, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT)
     p[i] = v;
+}
+
+// ------------------------------------------------------------------ GEMM operand staging
+// Row-major src [R, KR] (row stride KR) -> blocked dst (rows R, reduction KR),
+// zero padding to whole blocks; one thread per 8-element chunk of dst.
+__global__ __launch_bounds__(NT) void k_block_copy(const uint16_t* __restrict__ src,
+                                                   uint16_t* __restrict__ dst, int64_t R,
+                                                   int64_t KR, int64_t nkb, int64_t src_batch,
+                                                   int64_t dst_batch) {
+  const int64_t cpr = nkb * (arblk::KB / 8);                 // chunks per padded row
+  const int64_t total = arblk::row_tiles(R) * arblk::ROWS * cpr;
+  const int64_t b = blockIdx.y;
+  src += b * src_batch;
+  dst += b * dst_batch;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < total; i += (int64_t)gridDim.x * NT) {
+    const int64_t r = i / cpr, k = (i - r * cpr) * 8;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r < R && k < KR) v = *reinterpret_cast<const u32x4_t*>(src + r * KR + k);
+    *reinterpret_cast<u32x4_t*>(dst + arblk::chunk_offset(r, k, nkb)) = v;
+  }
+}
+
+// Row-major src [R, C] -> blocked dst with rows C and reduction R (a transpose),
+// zero padding; one thread per 8-element chunk of dst, consecutive threads on
+// consecutive src columns (coalesced reads).
+template <typename T>
+__global__ __launch_bounds__(NT) void k_block_transpose(const T* __restrict__ src, T* __restrict__ dst,
+                                                        int64_t R, int64_t C, int64_t nkb,
+                                                        int64_t src_batch, int64_t dst_batch) {
+  const int64_t rows = arblk::row_tiles(C) * arblk::ROWS;   // dst rows (padded)
+  const int64_t cpr = nkb * (arblk::KB / 8);
+  const int64_t total = rows * cpr;
+  const int64_t b = blockIdx.y;
+  src += b * src_batch;
+  dst += b * dst_batch;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < total; i += (int64_t)gridDim.x * NT) {
+    const int64_t kc = i / rows, c = i - kc * rows;          // dst row c fastest
+    const int64_t r0 = kc * 8;
+    T v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (c < C && r0 + e < R) ? src[(r0 + e) * C + c] : T(0);
+    T* d = dst + arblk::chunk_offset(c, r0, nkb);
+    if constexpr (sizeof(T) == 2) {
+      u32x4_t o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = (uint32_t)v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
+      *reinterpret_cast<u32x4_t*>(d) = o;
+    } else {
+      u32x4_t o0, o1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { o0[e] = v[e]; o1[e] = v[4 + e]; }
+      reinterpret_cast<u32x4_t*>(d)[0] = o0;
+      reinterpret_cast<u32x4_t*>(d)[1] = o1;
+    }
+  }
 }
 
 // ------------------------------------------------------------------ packing
@@ -421,12 +463,12 @@ ar_status fq_dispatch(FQArgs<WT, OT> a, int lpg, hipStream_t st) {
 
 template <typename WT, typename OT>
 ar_status fq_make(const void* W, const float* V, const float* alpha, const float* beta,
-                  float shrink, int64_t N, int64_t K, int g, ArGrid gr, void* Wq, uint8_t* codes,
-                  float* scale, uint8_t* zp, hipStream_t st) {
+                  float shrink, int64_t N, int64_t K, int g, ArGrid gr, void* Wq, int64_t wq_nkb,
+                  uint8_t* codes, float* scale, uint8_t* zp, hipStream_t st) {
   int lpg, E;
   ar_group_layout(g, &lpg, &E);
   FQArgs<WT, OT> a{static_cast<const WT*>(W), V, alpha, beta, shrink, N * (K / g), K, g,
-                   (int)(K / g), E, gr, static_cast<OT*>(Wq), codes, scale, zp};
+                   (int)(K / g), E, gr, static_cast<OT*>(Wq), wq_nkb, codes, scale, zp};
   return fq_dispatch(a, lpg, st);
 }
 
@@ -436,7 +478,7 @@ ar_status ste_make(const ArSteArgs& s, hipStream_t st) {
   ar_group_layout(s.g, &lpg, &E);
   SteK<WT> a{static_cast<const WT*>(s.W), s.V, s.alpha, s.beta, s.G, s.N * (s.K / s.g), s.K,
              s.g, (int)(s.K / s.g), E, s.gr, s.lr, s.mlr, s.clip_lo, s.clip_hi, s.flag,
-             s.bestV, s.bestA, s.bestB, s.gV, s.gA, s.gB, s.apply, s.Wq_next};
+             s.bestV, s.bestA, s.bestB, s.gV, s.gA, s.gB, s.apply, s.Wq_next, s.wq_nkb};
   const unsigned nb = blocks_for(a.ngroups * lpg);
   switch (lpg * 2 + (E == 1 ? 1 : 0)) {
 #define AR_STE_CASE(L)                                                                          \
@@ -456,16 +498,46 @@ ar_status ste_make(const ArSteArgs& s, hipStream_t st) {
 
 ar_status ar_launch_fakequant(int wdt, const void* W, const float* V, const float* alpha,
                               const float* beta, float shrink, int64_t N, int64_t K, int g,
-                              ArGrid gr, int out_dt, void* Wq, uint8_t* codes, float* scale,
-                              uint8_t* zp, hipStream_t st) {
+                              ArGrid gr, int out_dt, void* Wq, int64_t wq_nkb, uint8_t* codes,
+                              float* scale, uint8_t* zp, hipStream_t st) {
+  if (wq_nkb > 0 && out_dt != AR_BF16) return AR_ERR_INVALID_ARG;
   if (wdt == AR_BF16) {
     if (out_dt == AR_BF16)
-      return fq_make<uint16_t, uint16_t>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, codes, scale, zp, st);
-    return fq_make<uint16_t, float>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, codes, scale, zp, st);
+      return fq_make<uint16_t, uint16_t>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
+    return fq_make<uint16_t, float>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
   }
   if (out_dt == AR_BF16)
-    return fq_make<float, uint16_t>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, codes, scale, zp, st);
-  return fq_make<float, float>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, codes, scale, zp, st);
+    return fq_make<float, uint16_t>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
+  return fq_make<float, float>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
+}
+
+static unsigned stage_blocks(int64_t total) {
+  const int64_t want = (total + NT - 1) / NT;
+  return (unsigned)(want < 65536 ? want : 65536);
+}
+
+ar_status ar_launch_block_copy(const uint16_t* src, uint16_t* dst, int64_t batch, int64_t R,
+                               int64_t KR, int64_t nkb, hipStream_t st) {
+  const int64_t total = arblk::row_tiles(R) * arblk::ROWS * nkb * (arblk::KB / 8);
+  hipLaunchKernelGGL(k_block_copy, dim3(stage_blocks(total), (unsigned)batch), dim3(NT), 0, st,
+                     src, dst, R, KR, nkb, R * KR, arblk::row_tiles(R) * nkb * arblk::BLOCK_ELEMS);
+  return last_status();
+}
+
+ar_status ar_launch_block_transpose(const void* src, void* dst, int64_t batch, int64_t R,
+                                    int64_t C, int64_t nkb, int elem_bytes, hipStream_t st) {
+  const int64_t total = arblk::row_tiles(C) * arblk::ROWS * nkb * (arblk::KB / 8);
+  const int64_t dst_batch = arblk::row_tiles(C) * nkb * arblk::BLOCK_ELEMS;
+  const dim3 grid(stage_blocks(total), (unsigned)batch);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(k_block_transpose<uint16_t>, grid, dim3(NT), 0, st,
+                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C, nkb,
+                       R * C, dst_batch);
+  else
+    hipLaunchKernelGGL(k_block_transpose<uint32_t>, grid, dim3(NT), 0, st,
+                       static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), R, C, nkb,
+                       R * C, dst_batch);
+  return last_status();
 }
 
 ar_status ar_launch_ste_update(const ArSteArgs& s, hipStream_t st) {
@@ -477,18 +549,6 @@ ar_status ar_launch_loss_finalize(const float* partials, int nparts, double inv_
                                   hipStream_t st) {
   hipLaunchKernelGGL(k_loss_finalize, dim3(1), dim3(NT), 0, st, partials, nparts, inv_count,
                      loss_out, loss_slot, best_loss, flag);
-  return last_status();
-}
-
-ar_status ar_launch_transpose(const void* src, void* dst, int64_t batch, int64_t R, int64_t C,
-                              int elem_bytes, hipStream_t st) {
-  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64), (unsigned)batch);
-  if (elem_bytes == 2)
-    hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(NT), 0, st,
-                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C);
-  else
-    hipLaunchKernelGGL(k_transpose<uint32_t>, grid, dim3(NT), 0, st,
-                       static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), R, C);
   return last_status();
 }
 
