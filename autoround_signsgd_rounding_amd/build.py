@@ -1,6 +1,9 @@
 """Build libautoround_hip.so (gfx950) in-tree with hipcc.
 
-    python -m autoround_signsgd_rounding_amd.build
+    python autoround_signsgd_rounding_amd/build.py
+
+(run as a script, or through __graft_entry__.build(): importing the package
+loads the library being built).
 """
 import os
 import subprocess

@@ -68,7 +68,8 @@ struct GemmArgs {
 
 template <class Epi>
 __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+  // main-loop stages, then 16 bytes for the epilogue's per-wave sums
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES + 16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = wave >> 1, wj = wave & 1;
@@ -80,17 +81,31 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
   const __amdgpu_buffer_rsrc_t bufQ =
       make_rsrc(a.Q + (int64_t)tj * nk * arblk::BLOCK_ELEMS, (uint32_t)nk * OPB);
 
-  // load j (0..LPI-1) of step kt: operand j&1, 1 KiB piece wave*IPW + j/2 of the block.
-  // Steps past the end are issued out of range (zeros land in a stage nobody reads).
+  // Load j (0..LPI-1) of step kt: operand j&1, 1 KiB piece wave*IPW + j/2 of its block.
   const uint32_t lane_off = (uint32_t)(wave * IPW * 1024 + lane * 16);
-  auto issue = [&](int kt, int j) {
-    uint8_t* s = lds + (kt % NSTAGE) * STAGE_BYTES + (wave * IPW + (j >> 1)) * 1024;
-    const uint32_t vo = kt < nk ? lane_off + (uint32_t)(j >> 1) * 1024u : kOOB;
+  auto lds_dst = [&](int kt, int j) -> uint8_t* {
+    return lds + (kt % NSTAGE) * STAGE_BYTES + ((j & 1) ? OPB : 0) + (wave * IPW + (j >> 1)) * 1024;
+  };
+#define AR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+  auto issue_main = [&](int kt, int j) {   // kt < nk
+    const uint32_t vo = lane_off + (uint32_t)(j >> 1) * 1024u;
     const uint32_t so = (uint32_t)kt * OPB;
     if (j & 1)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(bufQ, (__attribute__((address_space(3))) void*)(s + OPB), 16, vo, so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bufQ, AR_LDS(lds_dst(kt, j)), 16, vo, so, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(bufP, (__attribute__((address_space(3))) void*)s, 16, vo, so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bufP, AR_LDS(lds_dst(kt, j)), 16, vo, so, 0, 0);
+  };
+  // kt >= nk: the freed stage takes piece kt-nk of the epilogue's prefetch (piece j lands
+  // in stage (nk + j) % NSTAGE); without a prefetch, an out-of-range load keeps the
+  // per-step load count uniform (zeros land in a stage nobody reads).
+  const __amdgpu_buffer_rsrc_t bufE =
+      make_rsrc(epi.prefetch_base(ti, tj), Epi::kPrefetch * (uint32_t)STAGE_BYTES);
+  auto issue_tail = [&](int kt, int j) {
+    const bool pf = Epi::kPrefetch > 0 && kt - nk < Epi::kPrefetch;
+    const uint32_t vo = pf ? lane_off + (uint32_t)(j >> 1) * 1024u + ((j & 1) ? (uint32_t)OPB : 0u)
+                           : kOOB;
+    const uint32_t so = pf ? (uint32_t)(kt - nk) * STAGE_BYTES : 0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(bufE, AR_LDS(lds_dst(kt, j)), 16, vo, so, 0, 0);
   };
 
   // fragment reads: lane reads row (lane & 31) of a 32-row block, logical chunk 2*ks + (lane >> 5)
@@ -117,7 +132,10 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
 #pragma unroll
   for (int p = 0; p < NSTAGE; ++p)
 #pragma unroll
-    for (int j = 0; j < LPI; ++j) issue(p, j);
+    for (int j = 0; j < LPI; ++j) {
+      if (p < nk) issue_main(p, j);
+      else issue_tail(p, j);
+    }
   wait_vm((NSTAGE - 1) * LPI);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -125,8 +143,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
   for (int idx = 0; idx < 8; ++idx) rd(0, 0, 0, idx);
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // substep 0 (fragments in buffer 0); read substep 1 into buffer 1
+  // one step: substep 0 (buffer 0) reads substep 1 into buffer 1; barrier; substep 1
+  // (buffer 1) reads step kt+1 substep 0 into buffer 0 and refills stage kt with step kt+4
+  auto step = [&](int kt, bool tail) {
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       acc[m >> 2][m & 3] =
@@ -141,21 +160,25 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
     wait_vm((NSTAGE - 2) * LPI);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // substep 1 (buffer 1); read step kt+1 substep 0 into buffer 0; refill stage kt with step kt+4
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       acc[m >> 2][m & 3] =
           __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[1][m >> 2], qf[1][m & 3], acc[m >> 2][m & 3], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       if (m & 1) rd(kt + 1, 0, 0, m >> 1);
-      else issue(kt + NSTAGE, m >> 1);
+      else if (tail) issue_tail(kt + NSTAGE, m >> 1);
+      else issue_main(kt + NSTAGE, m >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  int kt = 0;
+  for (; kt < nk - NSTAGE; ++kt) step(kt, false);
+  for (; kt < nk; ++kt) step(kt, true);
   wait_vm(0);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
-  epi(acc, ti, tj, wi, wj, lane, lds);
+  epi(acc, ti, tj, wi, wj, lane, lds, nk);
+#undef AR_LDS
 }
 
 // Accumulator element (bi, bj, r) of a lane sits at tile-local
@@ -166,16 +189,102 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
 // Forward epilogue: i = token t, j = output feature n. R = Y' - Y_true,
 // dYᵀ = bf16(R) into the blocked layout (rows n, reduction t), per-tile sum of R²
 // in a fixed order. Padding rows/columns give R = 0.
-template <typename YT>
-struct EpiFwd {
-  const YT* yB;      // targets, blocked like dYᵀ (rows n, reduction t), dtype YT
-  uint16_t* dyB;     // [tilesN][nkbT] blocks
-  float* partials;   // [tiles]
-  int nkbT;          // k-blocks along t
+//
+// bf16 targets: the tile's 8 target blocks (rows n, 256 t = 128 KiB, contiguous in
+// the blocked array) are prefetched into the four freed LDS stages during the last
+// main-loop steps; each lane turns its accumulators into R in place (8 bytes per
+// 4 tokens), then the workgroup streams the 128 KiB dYᵀ tile out with 16-byte
+// coalesced stores.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+struct EpiFwdBf16 {
+  static constexpr int kPrefetch = NSTAGE;     // 4 x 32 KiB = the whole target tile
+  const uint16_t* yB;   // targets, blocked like dYᵀ (rows n, reduction t)
+  uint16_t* dyB;
+  float* partials;
+  int nkbT;
   int tilesJ;
 
+  __device__ __forceinline__ const uint16_t* tile_base(const uint16_t* base, int ti, int tj) const {
+    return base + ((int64_t)tj * nkbT + (int64_t)ti * (BM / BK)) * arblk::BLOCK_ELEMS;
+  }
+  __device__ __forceinline__ const void* prefetch_base(int ti, int tj) const {
+    return tile_base(yB, ti, tj);
+  }
+  // LDS byte address of target/residual block q (0..7) of the tile
+  __device__ __forceinline__ uint32_t blk_lds(int q, int nk) const {
+    return (uint32_t)(((nk + (q >> 1)) % NSTAGE) * STAGE_BYTES + (q & 1) * OPB);
+  }
+
   __device__ __forceinline__ void operator()(f32x16_t (&acc)[4][4], int ti, int tj, int wi, int wj,
-                                             int lane, uint8_t* lds) const {
+                                             int lane, uint8_t* lds, int nk) const {
+    float* red = reinterpret_cast<float*>(lds + LDS_BYTES);
+    float sq = 0.0f;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int nl = wj * 128 + bj * 32 + (lane & 31);
+      const int nsw = (nl >> 2) & 3;
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int tl = wi * 128 + bi * 32 + q * 8 + (lane >> 5) * 4;   // tile-local token
+          const int c = (tl & 31) >> 3;
+          const uint32_t a = blk_lds(tl >> 5, nk) + (uint32_t)nl * ROWB +
+                             ((uint32_t)(c ^ nsw) << 4) + (uint32_t)(tl & 7) * 2u;
+          u32x2_t* p = reinterpret_cast<u32x2_t*>(lds + a);
+          const u32x2_t v = *p;
+          float y[4] = {__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
+                        __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
+          float r[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            r[e] = acc[bi][bj][q * 4 + e] - y[e];
+            sq += r[e] * r[e];
+          }
+          u32x2_t o;
+          o[0] = bf16_bits(r[0]) | (bf16_bits(r[1]) << 16);
+          o[1] = bf16_bits(r[2]) | (bf16_bits(r[3]) << 16);
+          *p = o;
+        }
+      }
+    }
+    sq = wave_sum(sq);
+    const int wave = wi * 2 + wj;
+    if (lane == 0) red[wave] = sq;
+    __syncthreads();
+    // stream the residual tile: 8 blocks x 16 KiB, contiguous in dyB
+    uint16_t* dst = const_cast<uint16_t*>(tile_base(dyB, ti, tj));
+    const int tid = wave * 64 + lane;
+#pragma unroll 4
+    for (int u = 0; u < (8 * arblk::BLOCK_BYTES) / (16 * NTHR); ++u) {
+      const int chunk = u * NTHR + tid;                 // 16-byte chunk of the tile
+      const int q = chunk >> 10;                        // 1024 chunks per block
+      const u32x4_t v =
+          *reinterpret_cast<const u32x4_t*>(lds + blk_lds(q, nk) + (uint32_t)(chunk & 1023) * 16u);
+      *reinterpret_cast<u32x4_t*>(dst + (int64_t)chunk * 8) = v;
+    }
+    if (wave == 0 && lane == 0) partials[ti * tilesJ + tj] = ((red[0] + red[1]) + red[2]) + red[3];
+  }
+};
+
+// float32 targets (float32 layers): read straight from the blocked array.
+struct EpiFwdF32 {
+  static constexpr int kPrefetch = 0;
+  const float* yB;
+  uint16_t* dyB;
+  float* partials;
+  int nkbT;
+  int tilesJ;
+
+  __device__ __forceinline__ const void* prefetch_base(int, int) const { return yB; }
+  __device__ __forceinline__ void operator()(f32x16_t (&acc)[4][4], int ti, int tj, int wi, int wj,
+                                             int lane, uint8_t* lds, int) const {
+    float* red = reinterpret_cast<float*>(lds + LDS_BYTES);
     float sq = 0.0f;
     const int64_t t0 = (int64_t)ti * BM, n0 = (int64_t)tj * BN;
 #pragma unroll
@@ -187,21 +296,11 @@ struct EpiFwd {
         for (int q = 0; q < 4; ++q) {
           const int64_t t = t0 + wi * 128 + bi * 32 + q * 8 + (lane >> 5) * 4;
           const int64_t off = arblk::offset(n, t, nkbT);
-          float y[4];
-          if constexpr (sizeof(YT) == 2) {
-            u32x2_t v = *reinterpret_cast<const u32x2_t*>(yB + off);
-            y[0] = __uint_as_float(v[0] << 16);
-            y[1] = __uint_as_float(v[0] & 0xFFFF0000u);
-            y[2] = __uint_as_float(v[1] << 16);
-            y[3] = __uint_as_float(v[1] & 0xFFFF0000u);
-          } else {
-            f32x4_t v = *reinterpret_cast<const f32x4_t*>(yB + off);
-            y[0] = v[0]; y[1] = v[1]; y[2] = v[2]; y[3] = v[3];
-          }
+          const f32x4_t v = *reinterpret_cast<const f32x4_t*>(yB + off);
           float r[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            r[e] = acc[bi][bj][q * 4 + e] - y[e];
+            r[e] = acc[bi][bj][q * 4 + e] - v[e];
             sq += r[e] * r[e];
           }
           u32x2_t o;
@@ -211,9 +310,7 @@ struct EpiFwd {
         }
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
-    float* red = reinterpret_cast<float*>(lds);
+    sq = wave_sum(sq);
     const int wave = wi * 2 + wj;
     if (lane == 0) red[wave] = sq;
     __syncthreads();
@@ -223,12 +320,14 @@ struct EpiFwd {
 
 // Gradient epilogue: i = output feature n, j = input feature k; G = scale * acc.
 struct EpiWgrad {
+  static constexpr int kPrefetch = 0;
   float* G;   // [N, K] row-major
   int64_t N, K;
   float scale;
 
+  __device__ __forceinline__ const void* prefetch_base(int, int) const { return G; }
   __device__ __forceinline__ void operator()(f32x16_t (&acc)[4][4], int ti, int tj, int wi, int wj,
-                                             int lane, uint8_t*) const {
+                                             int lane, uint8_t*, int) const {
     const int64_t n0 = (int64_t)ti * BM, k0 = (int64_t)tj * BN;
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj) {
@@ -262,11 +361,11 @@ ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void*
   const int nkbT = (int)(arblk::row_tiles(Tb) * (BM / BK));
   const int nwg = a.tilesI * a.tilesJ;
   if (ydt == AR_BF16) {
-    EpiFwd<uint16_t> e{static_cast<const uint16_t*>(yB), dyB, partials, nkbT, a.tilesJ};
-    hipLaunchKernelGGL(k_gemm<EpiFwd<uint16_t>>, dim3(nwg), dim3(NTHR), 0, st, a, e);
+    EpiFwdBf16 e{static_cast<const uint16_t*>(yB), dyB, partials, nkbT, a.tilesJ};
+    hipLaunchKernelGGL(k_gemm<EpiFwdBf16>, dim3(nwg), dim3(NTHR), 0, st, a, e);
   } else {
-    EpiFwd<float> e{static_cast<const float*>(yB), dyB, partials, nkbT, a.tilesJ};
-    hipLaunchKernelGGL(k_gemm<EpiFwd<float>>, dim3(nwg), dim3(NTHR), 0, st, a, e);
+    EpiFwdF32 e{static_cast<const float*>(yB), dyB, partials, nkbT, a.tilesJ};
+    hipLaunchKernelGGL(k_gemm<EpiFwdF32>, dim3(nwg), dim3(NTHR), 0, st, a, e);
   }
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
