@@ -52,6 +52,7 @@ class ArState(ctypes.Structure):
 
 class ArKernelTimes(ctypes.Structure):
     _fields_ = [
+        ("sample_every", ctypes.c_int32),
         ("fwd_gemm_ms", ctypes.c_double), ("wgrad_gemm_ms", ctypes.c_double),
         ("ste_update_ms", ctypes.c_double), ("loss_ms", ctypes.c_double),
         ("steps", ctypes.c_int64),
@@ -61,7 +62,7 @@ class ArKernelTimes(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m autoround_signsgd_rounding_amd.build` "
+            f"{LIB_PATH} is not built; run `python autoround_signsgd_rounding_amd/build.py` "
             "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -256,9 +257,10 @@ class TuneOutput:
 
 
 def tune_linear(W, X, Y, cfg: Config, *, want_state=True, want_wq=False, timed=False,
-                workspace=None, stream=None) -> TuneOutput:
+                time_every=1, workspace=None, stream=None) -> TuneOutput:
     """The whole tuning loop of one Linear (X [nsamples*seqlen, K] bf16,
-    Y [nsamples*seqlen, N] bf16/f32)."""
+    Y [nsamples*seqlen, N] bf16/f32). ``timed`` records HIP events around the
+    kernels of every ``time_every``-th step."""
     torch = _torch()
     _dev(W, X, Y)
     N, K = W.shape
@@ -278,6 +280,8 @@ def tune_linear(W, X, Y, cfg: Config, *, want_state=True, want_wq=False, timed=F
     b = torch.empty((N, G), dtype=torch.float32, device=dev) if want_state else None
     losses = torch.empty(max(cfg.iters, 1), dtype=torch.float32, device=dev)
     times = ArKernelTimes() if timed else None
+    if times is not None:
+        times.sample_every = time_every
     cc = cfg.c()
     _check(lib.ar_tune_linear(ctypes.byref(cc), _dt(W), _ptr(W), N, K, _ptr(X), _ptr(Y), ydt,
                               _ptr(codes), _ptr(scale), _ptr(zp), _ptr(Wq), _ptr(V), _ptr(a),

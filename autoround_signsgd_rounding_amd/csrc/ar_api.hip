@@ -348,9 +348,12 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t ysz = dsize(ydt);
 
+  // events around the kernels of every `every`-th step (8 per timed step)
+  const int every = (times && times->sample_every > 1) ? times->sample_every : 1;
+  const int ntimed = (times && c->iters > 0) ? (c->iters + every - 1) / every : 0;
   std::vector<hipEvent_t> ev;
-  if (times && c->iters > 0) {
-    ev.resize((size_t)c->iters * 8);
+  if (ntimed > 0) {
+    ev.resize((size_t)ntimed * 8);
     for (auto& e : ev) {
       if (hipEventCreate(&e) != hipSuccess) {
         e = nullptr;
@@ -394,7 +397,7 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
         static_cast<const uint8_t*>(w.YB) + (size_t)b * z.yb * ysz, ydt, Tb, w.WB, w.dyB, w.G,
         w.partials, w.flag, nullptr, losses ? losses + i : nullptr, w.best_loss, w.V, w.alpha,
         w.beta, w.bestV, w.bestA, w.bestB, nullptr, nullptr, nullptr, 1, true, st,
-        ev.empty() ? nullptr : &ev[(size_t)i * 8]));
+        (ntimed > 0 && i % every == 0) ? &ev[(size_t)(i / every) * 8] : nullptr));
   }
   // restore the best state and quantize it (the initial state when iters = 0)
   AR_TRY_C(ar_launch_fakequant(wdt, W, w.bestV, w.bestA, w.bestB, c->minmax_shrink, N, K, g, gr,
@@ -408,10 +411,12 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
       hipMemcpyAsync(beta_out, w.bestB, (size_t)N * Gn * 4, hipMemcpyDeviceToDevice, st))
     return cleanup(AR_ERR_HIP);
   if (times) {
+    const int32_t sample = times->sample_every;
     memset(times, 0, sizeof(*times));
-    if (!ev.empty()) {
+    times->sample_every = sample;
+    if (ntimed > 0) {
       if (hipStreamSynchronize(st) != hipSuccess) return cleanup(AR_ERR_HIP);
-      for (int i = 0; i < c->iters; ++i) {
+      for (int i = 0; i < ntimed; ++i) {
         float ms[4];
         for (int k = 0; k < 4; ++k)
           if (hipEventElapsedTime(&ms[k], ev[(size_t)i * 8 + 2 * k], ev[(size_t)i * 8 + 2 * k + 1]) !=
@@ -422,7 +427,7 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
         times->wgrad_gemm_ms += ms[2];
         times->ste_update_ms += ms[3];
       }
-      times->steps = c->iters;
+      times->steps = ntimed;
     }
   }
 #undef AR_TRY_C

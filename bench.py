@@ -29,6 +29,28 @@ import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COPY_BYTES = 1 << 30
+TIME_EVERY = 8              # HIP events around the kernels of every 8th SignSGD step
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_gemm_llama7b_q_proj.txt")
+GEMM_SOURCE = os.path.join(ROOT, "autoround_signsgd_rounding_amd", "csrc", "ar_gemm.hip")
+
+
+def _measured_traffic(workload):
+    """HBM bytes per launch of the forward GEMM from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs, or None when they were taken on another
+    workload or the GEMM source has changed since."""
+    import hashlib
+    if workload != "llama7b_q_proj" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if kv.get("gemm_source_sha256") != src:
+        return None
+    return int(float(kv["traffic_bytes"]))
 
 
 def _cpu_baseline(case, Yd, w, steps=2):
@@ -75,7 +97,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="llama7b_q_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the "
+                         "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 3}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the per-Linear tuning path runs on a single "
               "MI355X (multi-GPU sharding by output rows is a design note, not built)",
@@ -106,7 +140,8 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(times):
-        out = ar.tune_linear(W, X, Y, cfg, want_state=False, timed=True, workspace=ws)
+        out = ar.tune_linear(W, X, Y, cfg, want_state=False, timed=True,
+                             time_every=TIME_EVERY, workspace=ws)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -126,10 +161,11 @@ def main():
 
     iters_total = w.iters * args.steps
     value = iters_total / el
-    fwd_ms = sum(r[0].fwd_gemm_ms for r in recs) / iters_total
-    wgrad_ms = sum(r[0].wgrad_gemm_ms for r in recs) / iters_total
-    ste_ms = sum(r[0].ste_update_ms for r in recs) / iters_total
-    loss_ms = sum(r[0].loss_ms for r in recs) / iters_total
+    timed_steps = sum(r[0].steps for r in recs)
+    fwd_ms = sum(r[0].fwd_gemm_ms for r in recs) / timed_steps
+    wgrad_ms = sum(r[0].wgrad_gemm_ms for r in recs) / timed_steps
+    ste_ms = sum(r[0].ste_update_ms for r in recs) / timed_steps
+    loss_ms = sum(r[0].loss_ms for r in recs) / timed_steps
     pack_ms = sum(r[1].elapsed_time(r[2]) for r in recs) / args.steps
     gemm_flop = 2.0 * w.Tb * w.K * w.N
     kern = {"fwd_gemm": fwd_ms, "wgrad_gemm": wgrad_ms}
@@ -169,7 +205,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": _measured_traffic(w.name) if dom == "fwd_gemm" else None,
         },
         "detail": {
             "tflops_per_iter_effective": round(step_tflops, 1),
@@ -177,6 +213,8 @@ def main():
             "ms_per_iter": round(el / iters_total * 1e3, 4),
             "kernel_ms_per_iter": {"fwd_gemm": round(fwd_ms, 4), "wgrad_gemm": round(wgrad_ms, 4),
                                    "ste_update": round(ste_ms, 4), "loss": round(loss_ms, 4)},
+            "kernel_timing": f"HIP events around the kernels of every {TIME_EVERY}th step "
+                             f"({timed_steps} steps timed)",
             "fwd_gemm_tflops": round(gemm_flop / (fwd_ms * 1e-3) / 1e12, 1),
             "wgrad_gemm_tflops": round(gemm_flop / (wgrad_ms * 1e-3) / 1e12, 1),
             "pack_ms": round(pack_ms, 4),

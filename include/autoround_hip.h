@@ -69,14 +69,16 @@ typedef struct {
   float clip_hi;         /* alpha/beta upper clamp (default 1.0)                           */
 } ar_config;
 
-/* Per-kernel device time of one ar_tune_linear call (milliseconds, summed over
-   launches), measured with HIP events recorded on the call's stream. */
+/* Per-kernel device time of one ar_tune_linear call, measured with HIP events
+   recorded on the call's stream around the kernels of every sample_every-th
+   SignSGD step (milliseconds, summed over the timed steps). */
 typedef struct {
+  int32_t sample_every;  /* input: time steps i with i % sample_every == 0 (<= 1: every step) */
   double fwd_gemm_ms;    /* Y' = X_b·Ŵᵀ with residual / loss / dY epilogue */
   double wgrad_gemm_ms;  /* G = (2/(T_b·N))·dYᵀ·X_b                         */
   double ste_update_ms;  /* straight-through fold + SignSGD + next fake-quant */
   double loss_ms;        /* loss reduction + best-loss decision              */
-  int64_t steps;         /* number of SignSGD steps timed                    */
+  int64_t steps;         /* output: number of SignSGD steps timed            */
 } ar_kernel_times;
 
 /* Fill *cfg with the [LLMC] defaults: bits 4, group_size 128, asym, nsamples 128,
@@ -162,8 +164,9 @@ ar_status ar_tune_step(const ar_config* cfg, const ar_state* state, const uint16
    Outputs: codes [N, K] uint8, scale [N, G] float32, zp [N, G] uint8 (required);
    Wq [N, K] wdt (nullable); V_out [N, K], alpha_out/beta_out [N, G] float32 final
    (restored) state (nullable); losses [iters] float32 per-step loss (nullable).
-   ws: ar_workspace_size bytes. times: when non-NULL, per-kernel device times are
-   measured with HIP events and the call blocks until the stream has drained. */
+   ws: ar_workspace_size bytes. times: when non-NULL, per-kernel device times of
+   every times->sample_every-th step are measured with HIP events and the call
+   blocks until the stream has drained. */
 ar_status ar_tune_linear(const ar_config* cfg, int32_t wdt, const void* W, int64_t N, int64_t K,
                          const uint16_t* X, const void* Y, int32_t ydt, uint8_t* codes,
                          float* scale, uint8_t* zp, void* Wq, float* V_out, float* alpha_out,

@@ -146,3 +146,23 @@ def test_q_proj_200_iters_against_oracle_golden():
     assert abs(losses[0] - gl[0]) <= 1e-3 * gl[0]
     assert abs(losses.min() - float(gold["best_loss"])) <= 0.01 * float(gold["best_loss"])
     assert agree >= 0.999
+
+
+@pytest.mark.parametrize("every", [1, 3, 40])
+def test_timed_mode_samples_steps_and_changes_nothing(every):
+    """Event timing on every `every`-th step: the step count is ceil(iters /
+    every), every kernel time is positive, and the results are bit-identical to
+    an untimed run."""
+    w = synth.WORKLOADS["toy_256"]
+    case = synth.make_workload_case(w)
+    _, Yd = _targets(case)
+    cfg = _cfg(w)
+    Wd, Xd = weight_dev(case), bf16_dev(case.X_bits)
+    plain = ar.tune_linear(Wd, Xd, Yd, cfg)
+    timed = ar.tune_linear(Wd, Xd, Yd, cfg, timed=True, time_every=every)
+    torch.cuda.synchronize()
+    t = timed.times
+    assert t.steps == -(-cfg.iters // every) and t.sample_every == every
+    assert min(t.fwd_gemm_ms, t.wgrad_gemm_ms, t.ste_update_ms, t.loss_ms) > 0
+    for x, y in ((plain.codes, timed.codes), (plain.V, timed.V), (plain.losses, timed.losses)):
+        assert torch.equal(x, y)
