@@ -54,7 +54,7 @@ class ArKernelTimes(ctypes.Structure):
     _fields_ = [
         ("sample_every", ctypes.c_int32),
         ("fwd_gemm_ms", ctypes.c_double), ("wgrad_gemm_ms", ctypes.c_double),
-        ("ste_update_ms", ctypes.c_double), ("loss_ms", ctypes.c_double),
+        ("ste_update_ms", ctypes.c_double),
         ("steps", ctypes.c_int64),
     ]
 

@@ -171,28 +171,20 @@ ar_status check_loop_shape(const ar_config* c, int64_t N, int64_t K, int* g, int
     if (_s != AR_OK) return _s;        \
   } while (0)
 
-// Launches of one SignSGD step once the transposed minibatch is in place.
+// Launches of one SignSGD step once the transposed minibatch is in place:
+// forward product (residual, dY, per-tile sums of R²), gradient product (with
+// the loss and best-loss decision), straight-through update.
 ar_status enqueue_step(const ar_config* c, int wdt, const void* W, int64_t N, int64_t K, int g,
                        const uint16_t* XB, const uint16_t* XTB, const void* YB, int32_t ydt,
                        int64_t Tb, uint16_t* WB, uint16_t* dyB, float* G, float* partials,
-                       int* flag, float* loss_out, float* loss_slot, float* best_loss, float* V,
-                       float* alpha, float* beta, float* bestV, float* bestA, float* bestB,
-                       float* gV, float* gA, float* gB, int apply, bool write_next,
-                       hipStream_t st, hipEvent_t* ev /* 8 events or NULL */) {
+                       int* flag, float* loss_out, float* loss_slot, float* best_loss,
+                       float* V, float* alpha, float* beta, float* bestV,
+                       float* bestA, float* bestB, float* gV, float* gA, float* gB, int apply,
+                       bool write_next, hipStream_t st, hipEvent_t* ev /* 6 events or NULL */) {
   const double inv_count = 1.0 / ((double)Tb * (double)N);
   auto rec = [&](int k) {
     return (!ev || hipEventRecord(ev[k], st) == hipSuccess) ? AR_OK : AR_ERR_HIP;
   };
-  AR_TRY(rec(0));
-  AR_TRY(ar_launch_gemm_fwd(XB, WB, YB, ydt, dyB, partials, Tb, N, K, st));
-  AR_TRY(rec(1));
-  AR_TRY(rec(2));
-  AR_TRY(ar_launch_loss_finalize(partials, ar_fwd_tiles(Tb, N), inv_count, loss_out, loss_slot,
-                                 best_loss, flag, st));
-  AR_TRY(rec(3));
-  AR_TRY(rec(4));
-  AR_TRY(ar_launch_gemm_wgrad(dyB, XTB, G, N, K, Tb, (float)(2.0 * inv_count), st));
-  AR_TRY(rec(5));
   ArSteArgs s;
   s.wdt = wdt; s.W = W; s.V = V; s.alpha = alpha; s.beta = beta; s.G = G;
   s.N = N; s.K = K; s.g = g; s.gr = grid_of(c);
@@ -201,9 +193,19 @@ ar_status enqueue_step(const ar_config* c, int wdt, const void* W, int64_t N, in
   s.gV = gV; s.gA = gA; s.gB = gB; s.apply = apply;
   s.Wq_next = write_next ? WB : nullptr;
   s.wq_nkb = arblk::k_blocks(K);
-  AR_TRY(rec(6));
+  ArLossIn li;
+  li.partials = partials; li.nparts = ar_fwd_tiles(Tb, N); li.inv_count = inv_count;
+  li.loss_out = loss_out; li.loss_slot = loss_slot; li.best_loss = best_loss; li.flag = flag;
+
+  AR_TRY(rec(0));
+  AR_TRY(ar_launch_gemm_fwd(XB, WB, YB, ydt, dyB, partials, Tb, N, K, st));
+  AR_TRY(rec(1));
+  AR_TRY(rec(2));
+  AR_TRY(ar_launch_gemm_wgrad(dyB, XTB, G, N, K, Tb, (float)(2.0 * inv_count), li, st));
+  AR_TRY(rec(3));
+  AR_TRY(rec(4));
   AR_TRY(ar_launch_ste_update(s, st));
-  AR_TRY(rec(7));
+  AR_TRY(rec(5));
   return AR_OK;
 }
 
@@ -348,12 +350,12 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t ysz = dsize(ydt);
 
-  // events around the kernels of every `every`-th step (8 per timed step)
+  // events around the kernels of every `every`-th step (6 per timed step)
   const int every = (times && times->sample_every > 1) ? times->sample_every : 1;
   const int ntimed = (times && c->iters > 0) ? (c->iters + every - 1) / every : 0;
   std::vector<hipEvent_t> ev;
   if (ntimed > 0) {
-    ev.resize((size_t)ntimed * 8);
+    ev.resize((size_t)ntimed * 6);
     for (auto& e : ev) {
       if (hipEventCreate(&e) != hipSuccess) {
         e = nullptr;
@@ -397,7 +399,7 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
         static_cast<const uint8_t*>(w.YB) + (size_t)b * z.yb * ysz, ydt, Tb, w.WB, w.dyB, w.G,
         w.partials, w.flag, nullptr, losses ? losses + i : nullptr, w.best_loss, w.V, w.alpha,
         w.beta, w.bestV, w.bestA, w.bestB, nullptr, nullptr, nullptr, 1, true, st,
-        (ntimed > 0 && i % every == 0) ? &ev[(size_t)(i / every) * 8] : nullptr));
+        (ntimed > 0 && i % every == 0) ? &ev[(size_t)(i / every) * 6] : nullptr));
   }
   // restore the best state and quantize it (the initial state when iters = 0)
   AR_TRY_C(ar_launch_fakequant(wdt, W, w.bestV, w.bestA, w.bestB, c->minmax_shrink, N, K, g, gr,
@@ -417,15 +419,14 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
     if (ntimed > 0) {
       if (hipStreamSynchronize(st) != hipSuccess) return cleanup(AR_ERR_HIP);
       for (int i = 0; i < ntimed; ++i) {
-        float ms[4];
-        for (int k = 0; k < 4; ++k)
-          if (hipEventElapsedTime(&ms[k], ev[(size_t)i * 8 + 2 * k], ev[(size_t)i * 8 + 2 * k + 1]) !=
+        float ms[3];
+        for (int k = 0; k < 3; ++k)
+          if (hipEventElapsedTime(&ms[k], ev[(size_t)i * 6 + 2 * k], ev[(size_t)i * 6 + 2 * k + 1]) !=
               hipSuccess)
             return cleanup(AR_ERR_HIP);
         times->fwd_gemm_ms += ms[0];
-        times->loss_ms += ms[1];
-        times->wgrad_gemm_ms += ms[2];
-        times->ste_update_ms += ms[3];
+        times->wgrad_gemm_ms += ms[1];
+        times->ste_update_ms += ms[2];
       }
       times->steps = ntimed;
     }

@@ -143,6 +143,24 @@ __device__ __forceinline__ QE quant_elem(float w, float v, const QP& p, const Gr
   return e;
 }
 
+// ---------------------------------------------------------------- loss reduction
+// Sum of n float32 partials in float64 by a block of 256 threads, in a fixed
+// order: thread t adds partials t, t+256, ... in turn, then a pairwise tree
+// over the 256 sums. Every thread of the block calls it; all get the total.
+// sh: 256 doubles of LDS.
+__device__ __forceinline__ double block_sum_f64(const float* partials, int n, double* sh) {
+  const int t = threadIdx.x;
+  double acc = 0.0;
+  for (int i = t; i < n; i += 256) acc += (double)partials[i];
+  sh[t] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (t < s) sh[t] += sh[t + s];
+    __syncthreads();
+  }
+  return sh[0];
+}
+
 __device__ __forceinline__ float sgnf(float x) {
   return (x > 0.0f) ? 1.0f : ((x < 0.0f) ? -1.0f : 0.0f);
 }

@@ -31,6 +31,9 @@ constexpr int STAGE_BYTES = 2 * OPB;                // 32 KiB
 constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;     // 128 KiB
 constexpr int IPW = OPB / 1024 / 4;                 // 1 KiB loads per operand per wave (4)
 constexpr int LPI = 2 * IPW;                        // loads per wave per step (8)
+// LDS past the stages: per-wave sums of the forward epilogue (16 B), the loss
+// reduction's 256 doubles (at +64)
+constexpr int EXTRA_BYTES = 64 + 256 * 8;
 
 __device__ __forceinline__ void wait_vm(int n) {
   // s_waitcnt vmcnt(n) leaving the other counters unconstrained
@@ -68,8 +71,7 @@ struct GemmArgs {
 
 template <class Epi>
 __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
-  // main-loop stages, then 16 bytes for the epilogue's per-wave sums
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES + 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES + EXTRA_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wi = wave >> 1, wj = wave & 1;
@@ -136,6 +138,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
       if (p < nk) issue_main(p, j);
       else issue_tail(p, j);
     }
+  epi.pre(lds + LDS_BYTES);   // runs while the first stages load
   wait_vm((NSTAGE - 1) * LPI);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -215,6 +218,7 @@ struct EpiFwdBf16 {
   __device__ __forceinline__ const void* prefetch_base(int ti, int tj) const {
     return tile_base(yB, ti, tj);
   }
+  __device__ __forceinline__ void pre(uint8_t*) const {}
   // LDS byte address of target/residual block q (0..7) of the tile
   __device__ __forceinline__ uint32_t blk_lds(int q, int nk) const {
     return (uint32_t)(((nk + (q >> 1)) % NSTAGE) * STAGE_BYTES + (q & 1) * OPB);
@@ -282,6 +286,7 @@ struct EpiFwdF32 {
   int tilesJ;
 
   __device__ __forceinline__ const void* prefetch_base(int, int) const { return yB; }
+  __device__ __forceinline__ void pre(uint8_t*) const {}
   __device__ __forceinline__ void operator()(f32x16_t (&acc)[4][4], int ti, int tj, int wi, int wj,
                                              int lane, uint8_t* lds, int) const {
     float* red = reinterpret_cast<float*>(lds + LDS_BYTES);
@@ -318,14 +323,34 @@ struct EpiFwdF32 {
   }
 };
 
+// Loss of the step and the best-loss decision (see ArLossIn), reduced by the
+// gradient product's workgroup 0 while its first stages load.
+__device__ __forceinline__ void loss_pre(const ArLossIn& L, uint8_t* extra) {
+  if (blockIdx.x != 0) return;
+  const double total = block_sum_f64(L.partials, L.nparts, reinterpret_cast<double*>(extra + 64));
+  if (threadIdx.x == 0) {
+    const float loss = (float)(total * L.inv_count);
+    if (L.loss_out) *L.loss_out = loss;
+    if (L.loss_slot) *L.loss_slot = loss;
+    int imp = 0;
+    if (L.best_loss) {
+      imp = loss < *L.best_loss;
+      if (imp) *L.best_loss = loss;
+    }
+    *L.flag = imp;
+  }
+}
+
 // Gradient epilogue: i = output feature n, j = input feature k; G = scale * acc.
 struct EpiWgrad {
   static constexpr int kPrefetch = 0;
   float* G;   // [N, K] row-major
   int64_t N, K;
   float scale;
+  ArLossIn loss;
 
   __device__ __forceinline__ const void* prefetch_base(int, int) const { return G; }
+  __device__ __forceinline__ void pre(uint8_t* extra) const { loss_pre(loss, extra); }
   __device__ __forceinline__ void operator()(f32x16_t (&acc)[4][4], int ti, int tj, int wi, int wj,
                                              int lane, uint8_t*, int) const {
     const int64_t n0 = (int64_t)ti * BM, k0 = (int64_t)tj * BN;
@@ -371,13 +396,14 @@ ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void*
 }
 
 ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* G, int64_t N,
-                               int64_t K, int64_t Tb, float scale, hipStream_t st) {
+                               int64_t K, int64_t Tb, float scale, const ArLossIn& loss,
+                               hipStream_t st) {
   GemmArgs a;
   a.P = dyB; a.Q = XTB;
   a.nkb = (int)(arblk::row_tiles(Tb) * (BM / BK));
   a.tilesI = (int)arblk::row_tiles(N);
   a.tilesJ = (int)arblk::row_tiles(K);
-  EpiWgrad e{G, N, K, scale};
+  EpiWgrad e{G, N, K, scale, loss};
   hipLaunchKernelGGL(k_gemm<EpiWgrad>, dim3(a.tilesI * a.tilesJ), dim3(NTHR), 0, st, a, e);
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }

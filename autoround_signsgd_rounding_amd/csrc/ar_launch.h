@@ -23,8 +23,24 @@ int ar_fwd_tiles(int64_t Tb, int64_t N);
 ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void* yB, int ydt,
                              uint16_t* dyB, float* partials, int64_t Tb, int64_t N, int64_t K,
                              hipStream_t st);
+// Loss of the step from the forward product's per-tile sums of R², reduced by
+// the gradient product's workgroup 0 (float64, fixed order) while its first
+// loads are in flight: loss = sum * inv_count, written to loss_out / loss_slot
+// (nullable); flag = (loss < *best_loss) with *best_loss lowered on
+// improvement, or flag = 0 when best_loss is NULL.
+struct ArLossIn {
+  const float* partials;
+  int nparts;
+  double inv_count;     // 1 / (Tb * N)
+  float* loss_out;
+  float* loss_slot;
+  float* best_loss;
+  int* flag;
+};
+// G = scale * dYᵀ·X_b, row-major [N, K].
 ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* G, int64_t N,
-                               int64_t K, int64_t Tb, float scale, hipStream_t st);
+                               int64_t K, int64_t Tb, float scale, const ArLossIn& loss,
+                               hipStream_t st);
 // blocked staging: batch of row-major [R, KR] -> blocked (rows R, reduction KR)
 ar_status ar_launch_block_copy(const uint16_t* src, uint16_t* dst, int64_t batch, int64_t R,
                                int64_t KR, int64_t nkb, hipStream_t st);
@@ -65,9 +81,6 @@ struct ArSteArgs {
 };
 ar_status ar_launch_ste_update(const ArSteArgs& a, hipStream_t st);
 
-ar_status ar_launch_loss_finalize(const float* partials, int nparts, double inv_count,
-                                  float* loss_out, float* loss_slot, float* best_loss, int* flag,
-                                  hipStream_t st);
 ar_status ar_launch_fill_f32(float* p, float v, int64_t n, hipStream_t st);
 ar_status ar_launch_pack(int bits, const uint8_t* codes, const uint8_t* zp, int64_t N, int64_t K,
                          int64_t G, int32_t* qweight, int32_t* qzeros, hipStream_t st);

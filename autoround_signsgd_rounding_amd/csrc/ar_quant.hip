@@ -1,9 +1,10 @@
 // Quantizer-side kernels of the tuning step (gfx950): fake-quant, the
-// straight-through fold + SignSGD update, loss finalisation, staging of the
-// GEMM operands into their blocked layout, and int32 packing. All HBM-bound; every group of g contiguous input channels of
-// one output row is handled by LPG consecutive lanes, each lane streaming
-// 8-element chunks (16 B of bf16 / 32 B of float32) so that a wave reads
-// contiguous, coalesced spans.
+// stand-alone straight-through fold + SignSGD update (for group sizes the
+// gradient product cannot fuse), staging of the GEMM operands into their
+// blocked layout, and int32 packing. All HBM-bound; every group of g
+// contiguous input channels of one output row is handled by LPG consecutive
+// lanes, each lane streaming 8-element chunks (16 B of bf16 / 32 B of float32)
+// so that a wave reads contiguous, coalesced spans.
 //
 // Sources: llm-compressor AutoRound page (paper-core equations for RTN, the
 // learnable offset and SignSGD; _fake_quantize_with_offset; the per-module
@@ -14,6 +15,7 @@
 #include "ar_blocked.h"
 #include "ar_device.h"
 #include "ar_launch.h"
+#include "ar_ste.h"
 
 void ar_group_layout(int g, int* lpg, int* chunks_per_lane) {
   const int chunks = g / 8;
@@ -26,8 +28,6 @@ void ar_group_layout(int g, int* lpg, int* chunks_per_lane) {
 namespace {
 
 constexpr int NT = 256;
-
-__device__ __forceinline__ Grid grid_of(const ArGrid& g) { return Grid{g.maxq, g.half, g.sym}; }
 
 // ------------------------------------------------------------------ fake-quant
 template <typename WT, typename OT>
@@ -98,89 +98,37 @@ __global__ __launch_bounds__(NT) void k_fakequant(FQArgs<WT, OT> a) {
   }
 }
 
-// ------------------------------------------------------------------ STE + SignSGD
-template <typename WT>
-struct SteK {
-  const WT* W;
-  float* V;
-  float* alpha;
-  float* beta;
-  const float* G;
-  int64_t ngroups, K;
-  int g, Gn, E;
-  ArGrid gr;
-  float lr, mlr, clip_lo, clip_hi;
-  const int* flag;
-  float* bestV;
-  float* bestA;
-  float* bestB;
-  float* gV;
-  float* gA;
-  float* gB;
-  int apply;
-  uint16_t* Wq_next;   // blocked GEMM layout (wq_nkb k-blocks)
-  int64_t wq_nkb;
-};
-
-// Straight-through sums of one chunk: A += G·((q - zp) - m·t), Bs += G·[not m].
-__device__ __forceinline__ void ste_accum(const float (&w)[8], const float (&v)[8],
-                                          const float (&g)[8], const QP& p, const Grid& gr,
-                                          float& A, float& Bs) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const QE e = quant_elem(w[i], v[i], p, gr);
-    const float d = (e.q - p.zp) - (e.m ? e.t : 0.0f);
-    A += g[i] * d;
-    if (!e.m) Bs += g[i];
-  }
-}
-
-// One step for the elements of one chunk: dL/dV = G·s·m, optional snapshot of
-// the pre-update offset, V <- clamp(V - lr·sgn(dL/dV), -0.5, 0.5), and the bf16
-// fake-quant of the updated state for the next forward product.
-template <typename WT>
-__device__ __forceinline__ void ste_finish(const SteK<WT>& a, int64_t n, int64_t off, const float (&w)[8],
-                                           const float (&v)[8], const float (&g)[8], const QP& p,
-                                           const QP& pn, const Grid& gr, bool snap) {
-  float gv[8], vn[8], wq[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const QE e = quant_elem(w[i], v[i], p, gr);
-    gv[i] = e.m ? g[i] * p.s : 0.0f;
-    const float sg = e.m ? sgnf(g[i]) : 0.0f;
-    vn[i] = a.apply ? fminf(fmaxf(v[i] - a.lr * sg, -0.5f), 0.5f) : v[i];
-    wq[i] = quant_elem(w[i], vn[i], pn, gr).what;
-  }
-  if (a.gV) store8(a.gV + off, gv);
-  if (snap) store8(a.bestV + off, v);
-  if (a.apply) store8(a.V + off, vn);
-  if (a.Wq_next) store8(a.Wq_next + arblk::chunk_offset(n, off - n * a.K, a.wq_nkb), wq);
-}
-
-// ONE: each lane holds exactly one chunk of its group (kept in registers
-// across the three phases); otherwise chunks are re-read per phase.
+// ONE: each lane holds exactly one chunk of its group (the whole step runs on
+// registers, shared with the gradient product's fused epilogue); otherwise
+// chunks are re-read per phase.
 template <typename WT, int LPG, bool ONE>
 __global__ __launch_bounds__(NT) void k_ste_update(SteK<WT> a) {
   const int64_t gid = ((int64_t)blockIdx.x * NT + threadIdx.x) / LPG;
   const int lig = threadIdx.x % LPG;
   if (gid >= a.ngroups) return;
-  const Grid gr = grid_of(a.gr);
   const int64_t n = gid / a.Gn;
   const int64_t base = n * a.K + (gid - n * a.Gn) * a.g;
-  const int E = ONE ? 1 : a.E;
   const int64_t off0 = base + 8 * lig;
+  const bool snap = a.flag != nullptr && *a.flag != 0;
+  if (ONE) {
+    float w[8], v[8], g[8];
+    load8(a.W + off0, w);
+    load8(a.V + off0, v);
+    load8(a.G + off0, g);
+    ste_one<WT, LPG>(a, snap, gid, n, off0, lig, w, v, g, true);
+    return;
+  }
+  const Grid gr = grid_of(a.gr);
 
   // phase 1: group min / max (the Min-Max range)
-  float w0[8], v0[8], g0[8];
   float mn = INFINITY, mx = -INFINITY;
-  for (int e = 0; e < E; ++e) {
+  for (int e = 0; e < a.E; ++e) {
     float w[8];
     load8(a.W + off0 + 8 * LPG * e, w);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       mn = fminf(mn, w[i]);
       mx = fmaxf(mx, w[i]);
-      if (ONE) w0[i] = w[i];
     }
   }
   mn = group_min<LPG>(mn);
@@ -190,95 +138,28 @@ __global__ __launch_bounds__(NT) void k_ste_update(SteK<WT> a) {
 
   // phase 2: straight-through sums over the group
   float A = 0.0f, Bs = 0.0f;
-  if (ONE) {
-    load8(a.V + off0, v0);
-    load8(a.G + off0, g0);
-    ste_accum(w0, v0, g0, p, gr, A, Bs);
-  } else {
-    for (int e = 0; e < E; ++e) {
-      float w[8], v[8], g[8];
-      const int64_t off = off0 + 8 * LPG * e;
-      load8(a.W + off, w);
-      load8(a.V + off, v);
-      load8(a.G + off, g);
-      ste_accum(w, v, g, p, gr, A, Bs);
-    }
+  for (int e = 0; e < a.E; ++e) {
+    float w[8], v[8], g[8];
+    const int64_t off = off0 + 8 * LPG * e;
+    load8(a.W + off, w);
+    load8(a.V + off, v);
+    load8(a.G + off, g);
+    ste_accum(w, v, g, p, gr, A, Bs);
   }
   A = group_sum<LPG>(A);
   Bs = group_sum<LPG>(Bs);
-
-  // clip-factor gradients (zero for a zero-range group)
-  float ga = 0.0f, gb = 0.0f;
-  if (!p.zero) {
-    if (gr.sym) {
-      const float damax = 2.0f * A / gr.maxq;
-      const bool to_alpha = fabsf(al * mn) > fabsf(be * mx);
-      ga = to_alpha ? damax * fabsf(mn) : 0.0f;
-      gb = to_alpha ? 0.0f : damax * fabsf(mx);
-    } else {
-      const float B = -p.s * Bs;
-      const float D = A + B * p.lo / (p.s * p.s);
-      const float dlo = -D / gr.maxq - B / p.s;
-      const float dhi = D / gr.maxq;
-      ga = (mn < 0.0f) ? dlo * mn : 0.0f;
-      gb = (mx > 0.0f) ? dhi * mx : 0.0f;
-    }
-  }
-  const bool snap = a.flag != nullptr && *a.flag != 0;
-  float an = al, bn = be;
-  if (a.apply) {
-    an = fminf(fmaxf(al - a.mlr * sgnf(ga), a.clip_lo), a.clip_hi);
-    bn = fminf(fmaxf(be - a.mlr * sgnf(gb), a.clip_lo), a.clip_hi);
-  }
-  if (lig == 0) {
-    if (a.gA) a.gA[gid] = ga;
-    if (a.gB) a.gB[gid] = gb;
-    if (snap) { a.bestA[gid] = al; a.bestB[gid] = be; }
-    if (a.apply) { a.alpha[gid] = an; a.beta[gid] = bn; }
-  }
+  float an, bn;
+  clip_update(a, snap, gid, lig, mn, mx, al, be, p, A, Bs, true, an, bn);
   const QP pn = group_qparams(mn, mx, an, bn, gr);
 
   // phase 3: offsets, snapshot, next fake-quant
-  if (ONE) {
-    ste_finish(a, n, off0, w0, v0, g0, p, pn, gr, snap);
-  } else {
-    for (int e = 0; e < E; ++e) {
-      float w[8], v[8], g[8];
-      const int64_t off = off0 + 8 * LPG * e;
-      load8(a.W + off, w);
-      load8(a.V + off, v);
-      load8(a.G + off, g);
-      ste_finish(a, n, off, w, v, g, p, pn, gr, snap);
-    }
-  }
-}
-
-// ------------------------------------------------------------------ loss
-// loss = (sum of per-tile sums of R²) / (Tb·N), summed in a fixed order in
-// float64; strict "<" against the best loss decides the snapshot.
-__global__ __launch_bounds__(NT) void k_loss_finalize(const float* partials, int nparts,
-                                                      double inv_count, float* loss_out,
-                                                      float* loss_slot, float* best_loss,
-                                                      int* flag) {
-  __shared__ double sh[NT];
-  double acc = 0.0;
-  for (int i = threadIdx.x; i < nparts; i += NT) acc += (double)partials[i];
-  sh[threadIdx.x] = acc;
-  __syncthreads();
-  for (int s = NT / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) sh[threadIdx.x] += sh[threadIdx.x + s];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const float L = (float)(sh[0] * inv_count);
-    if (loss_out) *loss_out = L;
-    if (loss_slot) *loss_slot = L;
-    int imp = 0;
-    if (best_loss) {
-      imp = L < *best_loss;
-      if (imp) *best_loss = L;
-    }
-    *flag = imp;
+  for (int e = 0; e < a.E; ++e) {
+    float w[8], v[8], g[8];
+    const int64_t off = off0 + 8 * LPG * e;
+    load8(a.W + off, w);
+    load8(a.V + off, v);
+    load8(a.G + off, g);
+    ste_finish(a, n, off, w, v, g, p, pn, gr, snap);
   }
 }
 
@@ -476,9 +357,7 @@ template <typename WT>
 ar_status ste_make(const ArSteArgs& s, hipStream_t st) {
   int lpg, E;
   ar_group_layout(s.g, &lpg, &E);
-  SteK<WT> a{static_cast<const WT*>(s.W), s.V, s.alpha, s.beta, s.G, s.N * (s.K / s.g), s.K,
-             s.g, (int)(s.K / s.g), E, s.gr, s.lr, s.mlr, s.clip_lo, s.clip_hi, s.flag,
-             s.bestV, s.bestA, s.bestB, s.gV, s.gA, s.gB, s.apply, s.Wq_next, s.wq_nkb};
+  const SteK<WT> a = ste_args<WT>(s, E);
   const unsigned nb = blocks_for(a.ngroups * lpg);
   switch (lpg * 2 + (E == 1 ? 1 : 0)) {
 #define AR_STE_CASE(L)                                                                          \
@@ -544,13 +423,6 @@ ar_status ar_launch_ste_update(const ArSteArgs& s, hipStream_t st) {
   return s.wdt == AR_BF16 ? ste_make<uint16_t>(s, st) : ste_make<float>(s, st);
 }
 
-ar_status ar_launch_loss_finalize(const float* partials, int nparts, double inv_count,
-                                  float* loss_out, float* loss_slot, float* best_loss, int* flag,
-                                  hipStream_t st) {
-  hipLaunchKernelGGL(k_loss_finalize, dim3(1), dim3(NT), 0, st, partials, nparts, inv_count,
-                     loss_out, loss_slot, best_loss, flag);
-  return last_status();
-}
 
 ar_status ar_launch_fill_f32(float* p, float v, int64_t n, hipStream_t st) {
   if (n <= 0) return AR_OK;

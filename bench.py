@@ -165,7 +165,6 @@ def main():
     fwd_ms = sum(r[0].fwd_gemm_ms for r in recs) / timed_steps
     wgrad_ms = sum(r[0].wgrad_gemm_ms for r in recs) / timed_steps
     ste_ms = sum(r[0].ste_update_ms for r in recs) / timed_steps
-    loss_ms = sum(r[0].loss_ms for r in recs) / timed_steps
     pack_ms = sum(r[1].elapsed_time(r[2]) for r in recs) / args.steps
     gemm_flop = 2.0 * w.Tb * w.K * w.N
     kern = {"fwd_gemm": fwd_ms, "wgrad_gemm": wgrad_ms}
@@ -212,7 +211,7 @@ def main():
             "mfma_peak_frac_effective": round(step_tflops / PEAK_BF16_TFLOPS, 4),
             "ms_per_iter": round(el / iters_total * 1e3, 4),
             "kernel_ms_per_iter": {"fwd_gemm": round(fwd_ms, 4), "wgrad_gemm": round(wgrad_ms, 4),
-                                   "ste_update": round(ste_ms, 4), "loss": round(loss_ms, 4)},
+                                   "ste_update": round(ste_ms, 4)},
             "kernel_timing": f"HIP events around the kernels of every {TIME_EVERY}th step "
                              f"({timed_steps} steps timed)",
             "fwd_gemm_tflops": round(gemm_flop / (fwd_ms * 1e-3) / 1e12, 1),

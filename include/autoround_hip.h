@@ -74,11 +74,11 @@ typedef struct {
    SignSGD step (milliseconds, summed over the timed steps). */
 typedef struct {
   int32_t sample_every;  /* input: time steps i with i % sample_every == 0 (<= 1: every step) */
-  double fwd_gemm_ms;    /* Y' = X_b·Ŵᵀ with residual / loss / dY epilogue */
-  double wgrad_gemm_ms;  /* G = (2/(T_b·N))·dYᵀ·X_b                         */
-  double ste_update_ms;  /* straight-through fold + SignSGD + next fake-quant */
-  double loss_ms;        /* loss reduction + best-loss decision              */
-  int64_t steps;         /* output: number of SignSGD steps timed            */
+  double fwd_gemm_ms;    /* Y' = X_b·Ŵᵀ with the residual / dY / R² epilogue               */
+  double wgrad_gemm_ms;  /* G = (2/(T_b·N))·dYᵀ·X_b, with the loss reduction and best-loss
+                            decision in its prologue                                        */
+  double ste_update_ms;  /* straight-through fold + SignSGD update + next fake-quant         */
+  int64_t steps;         /* output: number of SignSGD steps timed                          */
 } ar_kernel_times;
 
 /* Fill *cfg with the [LLMC] defaults: bits 4, group_size 128, asym, nsamples 128,

@@ -163,6 +163,6 @@ def test_timed_mode_samples_steps_and_changes_nothing(every):
     torch.cuda.synchronize()
     t = timed.times
     assert t.steps == -(-cfg.iters // every) and t.sample_every == every
-    assert min(t.fwd_gemm_ms, t.wgrad_gemm_ms, t.ste_update_ms, t.loss_ms) > 0
+    assert min(t.fwd_gemm_ms, t.wgrad_gemm_ms, t.ste_update_ms) > 0
     for x, y in ((plain.codes, timed.codes), (plain.V, timed.V), (plain.losses, timed.losses)):
         assert torch.equal(x, y)
