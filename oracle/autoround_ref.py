@@ -204,6 +204,43 @@ def forward_backward(Xb, Yb, what, *, amp: bool = True, n_scale: int | None = No
     return loss_sum / (T * Nn), G, loss_sum
 
 
+# ------------------------------------------------------------------ Gram form
+@dataclasses.dataclass
+class GramStats:
+    """Minibatch statistics of the Gram form: H = Xbᵀ·Xb [K, K], Cn = Eᵀ·Xb
+    [N, K] and e2 = sum(E²), where E = Xb·Wᵀ − Yb is the target's deviation from
+    the unquantized layer on these tokens. All float64."""
+    H: np.ndarray
+    Cn: np.ndarray
+    e2: float
+    T: int
+
+
+def gram_stats(Xb, Yb, W) -> GramStats:
+    """H = XᵀX is the weight of the layer-wise objective on the ADMM-Q page
+    ("1. 문제 공식화"); Cn and e2 carry the part of the target that the
+    unquantized weight does not reproduce (zero when Yb = Xb·Wᵀ exactly)."""
+    X64 = np.asarray(Xb, F64)
+    E = X64 @ np.asarray(W, F64).T - np.asarray(Yb, F64)
+    return GramStats(H=X64.T @ X64, Cn=E.T @ X64, e2=float(np.sum(E * E)), T=X64.shape[0])
+
+
+def forward_backward_gram(st: GramStats, W, what, *, n_scale: int | None = None):
+    """The loss and Ŵ-gradient of ``forward_backward`` (bf16 Ŵ operand),
+    evaluated through the minibatch's Gram matrix, with the residual kept
+    unrounded. With D = bf16(Ŵ) − W, the residual is R = Xb·Dᵀ + E, so
+      sum(R²)  = Σ D∘(D·H) + 2·Σ D∘Cn + e2,
+      dL/dŴ    = (2/(T·N))·Rᵀ·Xb = (2/(T·N))·(D·H + Cn).
+    float64. Returns (L, G[N, K], sum(R²))."""
+    N = what.shape[0]
+    Nn = N if n_scale is None else n_scale
+    D = bf16(what).astype(F64) - np.asarray(W, F64)
+    P = D @ st.H
+    loss_sum = float(np.sum(D * P) + 2.0 * np.sum(D * st.Cn) + st.e2)
+    G = (2.0 / (st.T * Nn)) * (P + st.Cn)
+    return loss_sum / (st.T * Nn), G, loss_sum
+
+
 # ------------------------------------------------------------------ S8
 def ste_grads(G, W, fq: FakeQuant, qp: QParams, wmin, wmax, alpha, beta,
               bits: int, sym: bool, group_size: int):
@@ -289,11 +326,16 @@ class StepResult:
 
 
 def tune_step(W, V, alpha, beta, wmin, wmax, Xb, Yb, cfg: Config, *, amp: bool = True,
-              n_scale: int | None = None) -> StepResult:
-    """One SignSGD iteration from state (V, alpha, beta) on one minibatch."""
+              n_scale: int | None = None, gram: GramStats | None = None) -> StepResult:
+    """One SignSGD iteration from state (V, alpha, beta) on one minibatch.
+    With ``gram`` (the minibatch's ``gram_stats``), loss and gradient come from
+    ``forward_backward_gram`` and Xb, Yb are not used."""
     qp = qparams(wmin, wmax, alpha, beta, cfg.bits, cfg.sym)
     fq = fake_quant(W, V, qp, cfg.bits, cfg.group_size)
-    L, G, loss_sum = forward_backward(Xb, Yb, fq.what, amp=amp, n_scale=n_scale)
+    if gram is not None:
+        L, G, loss_sum = forward_backward_gram(gram, W, fq.what, n_scale=n_scale)
+    else:
+        L, G, loss_sum = forward_backward(Xb, Yb, fq.what, amp=amp, n_scale=n_scale)
     gV, ga, gb = ste_grads(G, W, fq, qp, wmin, wmax, alpha, beta,
                            cfg.bits, cfg.sym, cfg.group_size)
     Vn, an, bn = signsgd_update(V, alpha, beta, gV, ga, gb, cfg)
@@ -334,17 +376,19 @@ def rtn_quant(W, cfg: Config):
 
 
 def tune_linear(W, minibatch, nb: int, cfg: Config, *, amp: bool = True,
-                n_scale: int | None = None, on_step=None) -> TuneResult:
+                n_scale: int | None = None, on_step=None, gram: bool = False) -> TuneResult:
     """The per-Linear tuning loop ([LLMC] tuning loop) with a best-loss snapshot.
 
     ``minibatch(b)`` returns (Xb, Yb) for minibatch b; step i uses
     b = i mod nb. The state (V, alpha, beta) whose loss is strictly below the
     best so far is snapshotted before its update; after ``iters`` steps the
     best state is restored and quantized. iters = 0 returns the initial state
-    (RTN with minmax_shrink).
+    (RTN with minmax_shrink). ``gram=True`` evaluates every step in the Gram
+    form (``forward_backward_gram``) from per-minibatch ``gram_stats``.
     """
     N, K = W.shape
     W = np.asarray(W, F32)
+    stats = {}
     wmin, wmax = group_minmax(W, cfg.group_size)
     V = np.zeros((N, K), F32)
     alpha = np.full(wmin.shape, F32(cfg.minmax_shrink), F32)
@@ -354,7 +398,13 @@ def tune_linear(W, minibatch, nb: int, cfg: Config, *, amp: bool = True,
     losses = []
     for i in range(cfg.iters):
         Xb, Yb = minibatch(i % nb)
-        r = tune_step(W, V, alpha, beta, wmin, wmax, Xb, Yb, cfg, amp=amp, n_scale=n_scale)
+        st = None
+        if gram:
+            if i % nb not in stats:
+                stats[i % nb] = gram_stats(Xb, Yb, W)
+            st = stats[i % nb]
+        r = tune_step(W, V, alpha, beta, wmin, wmax, Xb, Yb, cfg, amp=amp, n_scale=n_scale,
+                      gram=st)
         losses.append(r.loss)
         if r.loss < best_loss:
             best_loss, best_step = r.loss, i

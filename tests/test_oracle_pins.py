@@ -162,6 +162,75 @@ def test_loss_and_grad_gram_identity():
     np.testing.assert_allclose(G, 2.0 * dW @ H / (T * N), rtol=1e-9, atol=1e-15)
 
 
+def _gram_problem(seed=5, N=20, K=48, T=64, wdt="f32"):
+    """bf16 tokens, a target that the unquantized layer does not reproduce
+    exactly (bf16-rounded product plus noise), and an arbitrary state."""
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((N, K)) * 0.03).astype(F32)
+    if wdt == "bf16":
+        W = O.bf16(W)
+    X = O.bf16(rng.standard_normal((T, K)).astype(F32))
+    Y = O.bf16((X.astype(np.float64) @ W.astype(np.float64).T
+                + 0.01 * rng.standard_normal((T, N))).astype(F32))
+    wmin, wmax = O.group_minmax(W, 8)
+    a = rng.uniform(0.6, 1.0, wmin.shape).astype(F32)
+    b = rng.uniform(0.6, 1.0, wmin.shape).astype(F32)
+    V = rng.uniform(-0.5, 0.5, (N, K)).astype(F32)
+    qp = O.qparams(wmin, wmax, a, b, 4, False)
+    fq = O.fake_quant(W, V, qp, 4, 8)
+    return W, X, Y, fq
+
+
+@pytest.mark.parametrize("wdt", ["f32", "bf16"])
+def test_gram_form_equals_token_form(wdt):
+    """The Gram form reproduces the token form of the same loss: with the bf16
+    operand Ŵ, R = Xb·bf16(Ŵ)ᵀ − Yb summed over tokens in float64 gives
+    sum(R²) and the gradient (2/(T·N))·Rᵀ·Xb."""
+    W, X, Y, fq = _gram_problem(wdt=wdt)
+    T, N = X.shape[0], W.shape[0]
+    R = X.astype(np.float64) @ O.bf16(fq.what).astype(np.float64).T - Y.astype(np.float64)
+    st = O.gram_stats(X, Y, W)
+    L, G, loss_sum = O.forward_backward_gram(st, W, fq.what)
+    np.testing.assert_allclose(loss_sum, np.sum(R * R), rtol=1e-10)
+    np.testing.assert_allclose(L, np.sum(R * R) / (T * N), rtol=1e-10)
+    Gt = 2.0 * R.T @ X.astype(np.float64) / (T * N)
+    assert np.abs(G - Gt).max() <= 1e-10 * np.abs(Gt).max()
+    # and the same loss as the token-form oracle (whose loss also keeps R unrounded)
+    L_tok, _, _ = O.forward_backward(X, Y, fq.what, amp=True)
+    np.testing.assert_allclose(L, L_tok, rtol=1e-10)
+
+
+def test_gram_stats_vanish_for_exact_targets():
+    """Yb = Xb·Wᵀ exactly: the target terms vanish and the loss is the
+    Hessian-weighted form Tr(D·H·Dᵀ)/(T·N) of the ADMM-Q page."""
+    W, X, _, fq = _gram_problem(seed=6)
+    Y = X.astype(np.float64) @ W.astype(np.float64).T
+    st = O.gram_stats(X, Y, W)
+    assert st.e2 == 0.0 and not st.Cn.any()
+    D = O.bf16(fq.what).astype(np.float64) - W.astype(np.float64)
+    T, N = X.shape[0], W.shape[0]
+    L, G, _ = O.forward_backward_gram(st, W, fq.what)
+    np.testing.assert_allclose(L, np.trace(D @ st.H @ D.T) / (T * N), rtol=1e-12)
+    np.testing.assert_allclose(st.H, st.H.T, rtol=0, atol=0)
+
+
+def test_gram_loop_first_loss_matches_token_loop():
+    """Both loop modes evaluate the same RTN state first, with the same
+    unrounded residual, so the first losses agree; every Gram-mode loss is
+    the token-form loss of the state it was taken at."""
+    W, X, Y = _full_batch_problem()
+    cfg = _cfg(bits=4, group_size=16, iters=12)
+    seen = []
+    r_g = O.tune_linear(W, lambda b: (X, Y), 1, cfg, gram=True,
+                        on_step=lambda i, r: seen.append(r.what))
+    r_t = O.tune_linear(W, lambda b: (X, Y), 1, cfg)
+    np.testing.assert_allclose(r_g.losses[0], r_t.losses[0], rtol=1e-10)
+    for L, what in zip(r_g.losses, seen):
+        Lt, _, _ = O.forward_backward(X, Y, what, amp=True)
+        np.testing.assert_allclose(L, Lt, rtol=1e-9)
+    assert r_g.best_loss == min(r_g.losses) and r_g.best_loss <= r_g.losses[0]
+
+
 def test_amp_close_to_exact():
     W, X, Y, wmin, wmax, a, b, V = _problem(K=64, T=64)
     qp = O.qparams(wmin, wmax, a, b, 3, False)
