@@ -26,6 +26,8 @@ STATUS = {
 EXPORTS = (
     "ar_config_default", "ar_status_string", "ar_workspace_size", "ar_step_workspace_size",
     "ar_rtn_quant", "ar_fakequant_fwd", "ar_tune_step", "ar_tune_linear", "ar_pack", "ar_unpack",
+    "ar_gram_workspace_size", "ar_gram_step_workspace_size", "ar_tune_step_gram",
+    "ar_tune_linear_gram",
 )
 
 
@@ -77,6 +79,12 @@ def _load():
                          vp, sz, vp],
         "ar_tune_linear": [cfgp, i32, vp, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                            vp, sz, ctypes.POINTER(ArKernelTimes), vp],
+        "ar_gram_workspace_size": [cfgp, i32, i64, i64, i32, ctypes.POINTER(sz)],
+        "ar_gram_step_workspace_size": [cfgp, i32, i64, i64, i64, i32, ctypes.POINTER(sz)],
+        "ar_tune_step_gram": [cfgp, ctypes.POINTER(ArState), vp, vp, i32, i64, vp, vp, vp, vp,
+                              i32, vp, sz, vp],
+        "ar_tune_linear_gram": [cfgp, i32, vp, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
+                                vp, vp, sz, ctypes.POINTER(ArKernelTimes), vp],
         "ar_pack": [i32, vp, vp, i64, i64, i64, vp, vp, vp],
         "ar_unpack": [i32, vp, vp, i64, i64, i64, vp, vp, vp],
     }
@@ -180,6 +188,22 @@ def step_workspace_size(cfg: Config, N: int, K: int, Tb: int, ydtype) -> int:
     return out.value
 
 
+def gram_workspace_size(cfg: Config, wdt: int, N: int, K: int, ydtype) -> int:
+    out = ctypes.c_size_t()
+    cc = cfg.c()
+    _check(lib.ar_gram_workspace_size(ctypes.byref(cc), wdt, N, K, ydtype, ctypes.byref(out)),
+           "ar_gram_workspace_size")
+    return out.value
+
+
+def gram_step_workspace_size(cfg: Config, wdt: int, N: int, K: int, Tb: int, ydtype) -> int:
+    out = ctypes.c_size_t()
+    cc = cfg.c()
+    _check(lib.ar_gram_step_workspace_size(ctypes.byref(cc), wdt, N, K, Tb, ydtype,
+                                           ctypes.byref(out)), "ar_gram_step_workspace_size")
+    return out.value
+
+
 def rtn_quant(W, cfg: Config, stream=None, want_wq: bool = True):
     """RTN codes [N,K] u8, scale [N,G] f32, zp [N,G] u8, Wq [N,K] (W's dtype)."""
     torch = _torch()
@@ -214,10 +238,11 @@ def fakequant_fwd(W, V, alpha, beta, cfg: Config, stream=None):
 
 
 def tune_step(W, V, alpha, beta, Xb, Yb, cfg: Config, *, best=None, want_grads=True,
-              apply_update=True, workspace=None, stream=None):
+              apply_update=True, workspace=None, stream=None, gram=False):
     """One SignSGD step in place on (V, alpha, beta). ``best`` is an optional
     tuple (best_V, best_alpha, best_beta, best_loss[1]). Returns
-    (loss[1] device tensor, gV, galpha, gbeta) with grads None unless wanted."""
+    (loss[1] device tensor, gV, galpha, gbeta) with grads None unless wanted.
+    ``gram`` selects ar_tune_step_gram."""
     torch = _torch()
     _dev(W, V, alpha, beta, Xb, Yb)
     N, K = W.shape
@@ -226,8 +251,9 @@ def tune_step(W, V, alpha, beta, Xb, Yb, cfg: Config, *, best=None, want_grads=T
         raise ValueError("Xb must be bf16 [Tb, K] and Yb [Tb, N]")
     ydt = _dt(Yb)
     if workspace is None:
-        workspace = torch.empty(step_workspace_size(cfg, N, K, Tb, ydt), dtype=torch.uint8,
-                                device=W.device)
+        need = gram_step_workspace_size(cfg, _dt(W), N, K, Tb, ydt) if gram else \
+            step_workspace_size(cfg, N, K, Tb, ydt)
+        workspace = torch.empty(need, dtype=torch.uint8, device=W.device)
     loss = torch.empty(1, dtype=torch.float32, device=W.device)
     gV = torch.empty_like(V) if want_grads else None
     ga = torch.empty_like(alpha) if want_grads else None
@@ -237,9 +263,11 @@ def tune_step(W, V, alpha, beta, Xb, Yb, cfg: Config, *, best=None, want_grads=T
                  None if bV is None else bV.data_ptr(), None if bA is None else bA.data_ptr(),
                  None if bB is None else bB.data_ptr(), None if bL is None else bL.data_ptr())
     cc = cfg.c()
-    _check(lib.ar_tune_step(ctypes.byref(cc), ctypes.byref(st), _ptr(Xb), _ptr(Yb), ydt, Tb,
-                            _ptr(loss), _ptr(gV), _ptr(ga), _ptr(gb), int(apply_update),
-                            _ptr(workspace), workspace.numel(), _stream(stream)), "ar_tune_step")
+    fn, name = (lib.ar_tune_step_gram, "ar_tune_step_gram") if gram else \
+        (lib.ar_tune_step, "ar_tune_step")
+    _check(fn(ctypes.byref(cc), ctypes.byref(st), _ptr(Xb), _ptr(Yb), ydt, Tb, _ptr(loss),
+              _ptr(gV), _ptr(ga), _ptr(gb), int(apply_update), _ptr(workspace),
+              workspace.numel(), _stream(stream)), name)
     return loss, gV, ga, gb
 
 
@@ -257,10 +285,11 @@ class TuneOutput:
 
 
 def tune_linear(W, X, Y, cfg: Config, *, want_state=True, want_wq=False, timed=False,
-                time_every=1, workspace=None, stream=None) -> TuneOutput:
+                time_every=1, workspace=None, stream=None, gram=False) -> TuneOutput:
     """The whole tuning loop of one Linear (X [nsamples*seqlen, K] bf16,
     Y [nsamples*seqlen, N] bf16/f32). ``timed`` records HIP events around the
-    kernels of every ``time_every``-th step."""
+    kernels of every ``time_every``-th step. ``gram`` selects
+    ar_tune_linear_gram."""
     torch = _torch()
     _dev(W, X, Y)
     N, K = W.shape
@@ -270,7 +299,9 @@ def tune_linear(W, X, Y, cfg: Config, *, want_state=True, want_wq=False, timed=F
     ydt = _dt(Y)
     dev = W.device
     if workspace is None:
-        workspace = torch.empty(workspace_size(cfg, N, K, ydt), dtype=torch.uint8, device=dev)
+        need = gram_workspace_size(cfg, _dt(W), N, K, ydt) if gram else \
+            workspace_size(cfg, N, K, ydt)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     codes = torch.empty((N, K), dtype=torch.uint8, device=dev)
     scale = torch.empty((N, G), dtype=torch.float32, device=dev)
     zp = torch.empty((N, G), dtype=torch.uint8, device=dev)
@@ -283,11 +314,12 @@ def tune_linear(W, X, Y, cfg: Config, *, want_state=True, want_wq=False, timed=F
     if times is not None:
         times.sample_every = time_every
     cc = cfg.c()
-    _check(lib.ar_tune_linear(ctypes.byref(cc), _dt(W), _ptr(W), N, K, _ptr(X), _ptr(Y), ydt,
-                              _ptr(codes), _ptr(scale), _ptr(zp), _ptr(Wq), _ptr(V), _ptr(a),
-                              _ptr(b), _ptr(losses), _ptr(workspace), workspace.numel(),
-                              ctypes.byref(times) if timed else None, _stream(stream)),
-           "ar_tune_linear")
+    fn, name = (lib.ar_tune_linear_gram, "ar_tune_linear_gram") if gram else \
+        (lib.ar_tune_linear, "ar_tune_linear")
+    _check(fn(ctypes.byref(cc), _dt(W), _ptr(W), N, K, _ptr(X), _ptr(Y), ydt, _ptr(codes),
+              _ptr(scale), _ptr(zp), _ptr(Wq), _ptr(V), _ptr(a), _ptr(b), _ptr(losses),
+              _ptr(workspace), workspace.numel(), ctypes.byref(times) if timed else None,
+              _stream(stream)), name)
     return TuneOutput(codes, scale, zp, Wq, V, a, b, losses[:cfg.iters], times)
 
 

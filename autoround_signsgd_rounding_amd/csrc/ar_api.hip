@@ -150,6 +150,73 @@ LoopWs carve_loop(void* ws, int64_t N, int64_t K, int64_t nb, int64_t Tb, int64_
   return w;
 }
 
+// Gram form: blocked element counts and workspace.
+struct GramSizes {
+  int nred;              // 1 (bf16 W) or 2 (float32 W as W_hi + W_lo) reduction segments of K
+  int64_t nkbR, nkb3;    // k-blocks of the statistics product (nred·K) and of D·H (3K)
+  int64_t xb2, wb2, hb, db, fsz;
+  GramSizes(int wdt, int64_t N, int64_t K, int64_t Tb) {
+    nred = wdt == AR_F32 ? 2 : 1;
+    nkbR = arblk::k_blocks(nred * K);
+    nkb3 = arblk::k_blocks(3 * K);
+    xb2 = arblk::row_tiles(Tb) * nkbR * arblk::BLOCK_ELEMS;
+    wb2 = arblk::row_tiles(N) * nkbR * arblk::BLOCK_ELEMS;
+    hb = arblk::row_tiles(K) * nkb3 * arblk::BLOCK_ELEMS;
+    db = arblk::row_tiles(N) * nkb3 * arblk::BLOCK_ELEMS;
+    fsz = (N > K ? N : K) * K;
+  }
+};
+
+struct GramWs {
+  uint16_t* XTB;   // nb minibatches, rows K, reduction Tb
+  uint16_t* HB;    // nb x [H_hi | H_lo | H_hi]
+  float* Cn;       // nb x [N, K]
+  double* e2;      // nb
+  uint16_t* XB2;   // staging: [X_b] or [X_b | X_b], rows Tb
+  void* YB;        // staging: Y_b, rows N, reduction Tb
+  uint16_t* dyB;   // staging: bf16(X_b·Wᵀ - Y_b), rows N, reduction Tb
+  uint16_t* WB2;   // [W] or [W_hi | W_lo], rows N
+  float* F;        // H of a minibatch (staging), then P = D·H (loop)
+  float* fwd_partials;
+  uint16_t* DB;    // [D_hi | D_hi | D_lo], rows N
+  float *V[2], *A[2], *B[2];
+  float *bestV, *bestA, *bestB;
+  float* partials;
+  float* best_loss;
+  int* flag;
+};
+GramWs carve_gram(void* ws, int wdt, int64_t N, int64_t K, int64_t nb, int64_t Tb, int64_t Gn,
+                  int g, int32_t ydt, size_t* bytes) {
+  Carver c{static_cast<uint8_t*>(ws)};
+  const BlkSizes z(N, K, Tb);
+  const GramSizes q(wdt, N, K, Tb);
+  GramWs w;
+  w.XTB = c.take<uint16_t>((size_t)nb * z.xtb * 2);
+  w.HB = c.take<uint16_t>((size_t)nb * q.hb * 2);
+  w.Cn = c.take<float>((size_t)nb * N * K * 4);
+  w.e2 = c.take<double>((size_t)nb * 8);
+  w.XB2 = c.take<uint16_t>((size_t)q.xb2 * 2);
+  w.YB = c.take<uint8_t>((size_t)z.yb * dsize(ydt));
+  w.dyB = c.take<uint16_t>((size_t)z.yb * 2);
+  w.WB2 = c.take<uint16_t>((size_t)q.wb2 * 2);
+  w.F = c.take<float>((size_t)q.fsz * 4);
+  w.fwd_partials = c.take<float>((size_t)ar_fwd_tiles(Tb, N) * 4);
+  w.DB = c.take<uint16_t>((size_t)q.db * 2);
+  for (int i = 0; i < 2; ++i) {
+    w.V[i] = c.take<float>((size_t)N * K * 4);
+    w.A[i] = c.take<float>((size_t)N * Gn * 4);
+    w.B[i] = c.take<float>((size_t)N * Gn * 4);
+  }
+  w.bestV = c.take<float>((size_t)N * K * 4);
+  w.bestA = c.take<float>((size_t)N * Gn * 4);
+  w.bestB = c.take<float>((size_t)N * Gn * 4);
+  w.partials = c.take<float>((size_t)ar_gram_partials(N, K, g) * 4);
+  w.best_loss = c.take<float>(16);
+  w.flag = c.take<int>(16);
+  *bytes = c.off;
+  return w;
+}
+
 ar_status check_loop_shape(const ar_config* c, int64_t N, int64_t K, int* g, int64_t* M,
                            int64_t* Tb) {
   ar_status s = check_quant(c, N, K, g);
@@ -193,7 +260,7 @@ ar_status enqueue_step(const ar_config* c, int wdt, const void* W, int64_t N, in
   s.gV = gV; s.gA = gA; s.gB = gB; s.apply = apply;
   s.Wq_next = write_next ? WB : nullptr;
   s.wq_nkb = arblk::k_blocks(K);
-  ArLossIn li;
+  ArLossIn li{};
   li.partials = partials; li.nparts = ar_fwd_tiles(Tb, N); li.inv_count = inv_count;
   li.loss_out = loss_out; li.loss_slot = loss_slot; li.best_loss = best_loss; li.flag = flag;
 
@@ -207,6 +274,53 @@ ar_status enqueue_step(const ar_config* c, int wdt, const void* W, int64_t N, in
   AR_TRY(ar_launch_ste_update(s, st));
   AR_TRY(rec(5));
   return AR_OK;
+}
+
+// Statistics of minibatch b (H_b, Cn_b, e2_b) from its token-major rows Xb,
+// transposed rows XTB_b and targets Yb; XB2 / HB_b padding must already be zero.
+ar_status stage_gram_minibatch(const GramWs& w, const GramSizes& q, int64_t N, int64_t K,
+                               int64_t Tb, const uint16_t* Xb, const uint16_t* XTBb,
+                               const void* Yb, int32_t ydt, uint16_t* HBb, float* Cnb, double* e2b,
+                               hipStream_t st) {
+  const int64_t nkbT = arblk::row_tiles(Tb) * (arblk::ROWS / arblk::KB);
+  for (int r = 0; r < q.nred; ++r)
+    AR_TRY(ar_launch_place(Xb, AR_BF16, Tb, K, w.XB2, q.nkbR, r * K, 0, st));
+  AR_TRY(ar_launch_block_transpose(Yb, w.YB, 1, Tb, N, nkbT, (int)dsize(ydt), st));
+  // dY = bf16(X_b·Wᵀ - Y_b), per-tile sums of its square
+  AR_TRY(ar_launch_gemm_fwd(w.XB2, w.WB2, w.YB, ydt, w.dyB, w.fwd_partials, Tb, N, q.nred * K,
+                            st));
+  // Cn = dYᵀ·X_b; e2 reduced by the product's workgroup 0
+  ArLossIn le{};
+  le.partials = w.fwd_partials; le.nparts = ar_fwd_tiles(Tb, N); le.inv_count = 1.0;
+  le.sum_out = e2b;
+  AR_TRY(ar_launch_gemm_f32out(w.dyB, XTBb, Cnb, N, K, nkbT, 1.0f, le, st));
+  // H = X_bᵀ·X_b, then its hi/lo operand [H_hi | H_lo | H_hi]
+  ArLossIn none{};
+  AR_TRY(ar_launch_gemm_f32out(XTBb, XTBb, w.F, K, K, nkbT, 1.0f, none, st));
+  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkb3, 0, 0, st));
+  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkb3, K, 1, st));
+  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkb3, 2 * K, 0, st));
+  return AR_OK;
+}
+
+// [W] or [W_hi | W_lo] operand of the statistics product (padding cleared).
+ar_status stage_gram_weight(const GramWs& w, const GramSizes& q, int wdt, const void* W,
+                            int64_t N, int64_t K, hipStream_t st) {
+  AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(w.WB2), 0.0f, q.wb2 / 2, st));
+  AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(w.XB2), 0.0f, q.xb2 / 2, st));
+  AR_TRY(ar_launch_place(W, wdt, N, K, w.WB2, q.nkbR, 0, 0, st));
+  if (q.nred == 2) AR_TRY(ar_launch_place(W, wdt, N, K, w.WB2, q.nkbR, K, 1, st));
+  return AR_OK;
+}
+
+ArGramArgs gram_args(const ar_config* c, int wdt, const void* W, int64_t N, int64_t K, int g,
+                     int64_t Tb) {
+  ArGramArgs a{};
+  a.wdt = wdt; a.W = W; a.N = N; a.K = K; a.g = g; a.gr = grid_of(c);
+  a.lr = c->lr; a.mlr = minmax_lr_of(c); a.clip_lo = c->clip_lo; a.clip_hi = c->clip_hi;
+  a.scale = (float)(2.0 / ((double)Tb * (double)N));
+  a.apply = 1;
+  return a;
 }
 
 }  // namespace
@@ -427,6 +541,227 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
         times->fwd_gemm_ms += ms[0];
         times->wgrad_gemm_ms += ms[1];
         times->ste_update_ms += ms[2];
+      }
+      times->steps = ntimed;
+    }
+  }
+#undef AR_TRY_C
+  return cleanup(AR_OK);
+}
+
+ar_status ar_gram_workspace_size(const ar_config* c, int32_t wdt, int64_t N, int64_t K,
+                                 int32_t ydt, size_t* bytes) {
+  int g;
+  int64_t M, Tb;
+  if (!bytes) return AR_ERR_INVALID_ARG;
+  AR_TRY(check_loop_shape(c, N, K, &g, &M, &Tb));
+  if (!dtype_ok(wdt) || !dtype_ok(ydt)) return AR_ERR_UNSUPPORTED;
+  carve_gram(nullptr, wdt, N, K, M / Tb, Tb, K / g, g, ydt, bytes);
+  return AR_OK;
+}
+
+ar_status ar_gram_step_workspace_size(const ar_config* c, int32_t wdt, int64_t N, int64_t K,
+                                      int64_t Tb, int32_t ydt, size_t* bytes) {
+  int g;
+  if (!bytes) return AR_ERR_INVALID_ARG;
+  AR_TRY(check_quant(c, N, K, &g));
+  if (N == 0 || K == 0 || Tb <= 0 || Tb % 8 != 0 || Tb >= kMaxLd) return AR_ERR_SHAPE;
+  if (!dtype_ok(wdt) || !dtype_ok(ydt)) return AR_ERR_UNSUPPORTED;
+  carve_gram(nullptr, wdt, N, K, 1, Tb, K / g, g, ydt, bytes);
+  return AR_OK;
+}
+
+ar_status ar_tune_step_gram(const ar_config* c, const ar_state* s, const uint16_t* Xb,
+                            const void* Yb, int32_t ydt, int64_t Tb, float* loss_out, float* gV,
+                            float* galpha, float* gbeta, int32_t apply_update, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (!s) return AR_ERR_INVALID_ARG;
+  int g;
+  AR_TRY(check_quant(c, s->N, s->K, &g));
+  AR_TRY(check_tune(c));
+  if (!dtype_ok(s->wdt) || !dtype_ok(ydt)) return AR_ERR_UNSUPPORTED;
+  if (g == 0 || Tb <= 0 || Tb % 8 != 0 || Tb >= kMaxLd) return AR_ERR_SHAPE;
+  const int nbest = (s->best_V != nullptr) + (s->best_alpha != nullptr) +
+                    (s->best_beta != nullptr) + (s->best_loss != nullptr);
+  if (nbest != 0 && nbest != 4) return AR_ERR_INVALID_ARG;
+  if (!s->W || !s->V || !s->alpha || !s->beta || !Xb || !Yb || !loss_out || !ws)
+    return AR_ERR_INVALID_ARG;
+  if (!a16(s->W) || !a16(s->V) || !a16(s->best_V) || !a16(Xb) || !a16(Yb) || !a16(gV) || !a16(ws))
+    return AR_ERR_INVALID_ARG;
+  const int64_t N = s->N, K = s->K, Gn = K / g;
+  size_t need;
+  carve_gram(nullptr, s->wdt, N, K, 1, Tb, Gn, g, ydt, &need);
+  if (ws_bytes < need) return AR_ERR_WORKSPACE;
+  GramWs w = carve_gram(ws, s->wdt, N, K, 1, Tb, Gn, g, ydt, &need);
+  const GramSizes q(s->wdt, N, K, Tb);
+  const BlkSizes z(N, K, Tb);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  AR_TRY(stage_gram_weight(w, q, s->wdt, s->W, N, K, st));
+  AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(w.HB), 0.0f, q.hb / 2, st));
+  AR_TRY(ar_launch_block_transpose(Xb, w.XTB, 1, Tb, K, z.nkbT, 2, st));
+  AR_TRY(stage_gram_minibatch(w, q, N, K, Tb, Xb, w.XTB, Yb, ydt, w.HB, w.Cn, w.e2, st));
+  // D of the current state, P = D·H, then the update into scratch buffers so the
+  // current state stays intact for the snapshot
+  AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(w.DB), 0.0f, q.db / 2, st));
+  AR_TRY(ar_launch_gram_d(s->wdt, s->W, s->V, s->alpha, s->beta, N, K, g, grid_of(c), w.DB, st));
+  ArLossIn none{};
+  AR_TRY(ar_launch_gemm_f32out(w.DB, w.HB, w.F, N, K, q.nkb3, 1.0f, none, st));
+  ArGramArgs a = gram_args(c, s->wdt, s->W, N, K, g, Tb);
+  a.Vc = s->V; a.Vn = w.V[0]; a.Ac = s->alpha; a.Bc = s->beta; a.An = w.A[0]; a.Bn = w.B[0];
+  a.P = w.F; a.Cn = w.Cn; a.apply = apply_update != 0; a.DB = w.DB; a.partials = w.partials;
+  a.gV = gV; a.gA = galpha; a.gB = gbeta;
+  AR_TRY(ar_launch_ste_gram(a, st));
+  ArLossIn li{};
+  li.partials = w.partials; li.nparts = (int)ar_gram_partials(N, K, g);
+  li.inv_count = 1.0 / ((double)Tb * (double)N); li.add = w.e2; li.loss_out = loss_out;
+  li.best_loss = s->best_loss; li.flag = w.flag;
+  AR_TRY(ar_launch_loss_reduce(li, st));
+  if (s->best_loss)
+    AR_TRY(ar_launch_gram_snapshot(w.flag, s->V, s->alpha, s->beta, s->best_V, s->best_alpha,
+                                   s->best_beta, N * K, N * Gn, st));
+  if (apply_update) {
+    if (hipMemcpyAsync(s->V, w.V[0], (size_t)N * K * 4, hipMemcpyDeviceToDevice, st) ||
+        hipMemcpyAsync(s->alpha, w.A[0], (size_t)N * Gn * 4, hipMemcpyDeviceToDevice, st) ||
+        hipMemcpyAsync(s->beta, w.B[0], (size_t)N * Gn * 4, hipMemcpyDeviceToDevice, st))
+      return AR_ERR_HIP;
+  }
+  return AR_OK;
+}
+
+ar_status ar_tune_linear_gram(const ar_config* c, int32_t wdt, const void* W, int64_t N,
+                              int64_t K, const uint16_t* X, const void* Y, int32_t ydt,
+                              uint8_t* codes, float* scale, uint8_t* zp, void* Wq, float* V_out,
+                              float* alpha_out, float* beta_out, float* losses, void* ws,
+                              size_t ws_bytes, ar_kernel_times* times, void* stream) {
+  int g;
+  int64_t M, Tb;
+  AR_TRY(check_loop_shape(c, N, K, &g, &M, &Tb));
+  if (!dtype_ok(wdt) || !dtype_ok(ydt)) return AR_ERR_UNSUPPORTED;
+  if (!W || !X || !Y || !codes || !scale || !zp || !ws) return AR_ERR_INVALID_ARG;
+  if (!a16(W) || !a16(X) || !a16(Y) || !a8(codes) || !a16(Wq) || !a16(V_out) || !a16(ws))
+    return AR_ERR_INVALID_ARG;
+  const int64_t Gn = K / g;
+  const int64_t nb = c->nsamples / c->batch_samples;
+  size_t need;
+  carve_gram(nullptr, wdt, N, K, nb, Tb, Gn, g, ydt, &need);
+  if (ws_bytes < need) return AR_ERR_WORKSPACE;
+  GramWs w = carve_gram(ws, wdt, N, K, nb, Tb, Gn, g, ydt, &need);
+  const GramSizes q(wdt, N, K, Tb);
+  const BlkSizes z(N, K, Tb);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t ysz = dsize(ydt);
+  const double inv_count = 1.0 / ((double)Tb * (double)N);
+  const int nparts = (int)ar_gram_partials(N, K, g);
+
+  // events around the two kernels of every `every`-th step
+  const int every = (times && times->sample_every > 1) ? times->sample_every : 1;
+  const int ntimed = (times && c->iters > 0) ? (c->iters + every - 1) / every : 0;
+  std::vector<hipEvent_t> ev;
+  if (ntimed > 0) {
+    ev.resize((size_t)ntimed * 4);
+    for (auto& e : ev) {
+      if (hipEventCreate(&e) != hipSuccess) {
+        e = nullptr;
+        for (auto& d : ev)
+          if (d) (void)hipEventDestroy(d);
+        return AR_ERR_HIP;
+      }
+    }
+  }
+  auto cleanup = [&](ar_status s) {
+    for (auto& e : ev) (void)hipEventDestroy(e);
+    return s;
+  };
+#define AR_TRY_C(expr)                   \
+  do {                                   \
+    ar_status _s = (expr);               \
+    if (_s != AR_OK) return cleanup(_s); \
+  } while (0)
+
+  // once per Linear: the statistics of every minibatch
+  AR_TRY_C(stage_gram_weight(w, q, wdt, W, N, K, st));
+  AR_TRY_C(ar_launch_fill_f32(reinterpret_cast<float*>(w.HB), 0.0f, nb * q.hb / 2, st));
+  AR_TRY_C(ar_launch_block_transpose(X, w.XTB, nb, Tb, K, z.nkbT, 2, st));
+  for (int64_t b = 0; b < nb; ++b)
+    AR_TRY_C(stage_gram_minibatch(w, q, N, K, Tb, X + b * Tb * K, w.XTB + b * z.xtb,
+                                  static_cast<const uint8_t*>(Y) + (size_t)b * Tb * N * ysz, ydt,
+                                  w.HB + b * q.hb, w.Cn + b * N * K, w.e2 + b, st));
+  // initial state, its D operand
+  AR_TRY_C(ar_launch_fill_f32(w.V[0], 0.0f, N * K, st));
+  AR_TRY_C(ar_launch_fill_f32(w.V[1], 0.0f, N * K, st));
+  AR_TRY_C(ar_launch_fill_f32(w.bestV, 0.0f, N * K, st));
+  for (float* p : {w.A[0], w.B[0], w.A[1], w.B[1], w.bestA, w.bestB})
+    AR_TRY_C(ar_launch_fill_f32(p, c->minmax_shrink, N * Gn, st));
+  AR_TRY_C(ar_launch_fill_f32(w.best_loss, INFINITY, 1, st));
+  AR_TRY_C(ar_launch_fill_f32(reinterpret_cast<float*>(w.flag), 0.0f, 1, st));
+  AR_TRY_C(ar_launch_fill_f32(reinterpret_cast<float*>(w.DB), 0.0f, q.db / 2, st));
+  const ArGrid gr = grid_of(c);
+  if (c->iters > 0)
+    AR_TRY_C(ar_launch_gram_d(wdt, W, w.V[0], w.A[0], w.B[0], N, K, g, gr, w.DB, st));
+
+  ArGramArgs a = gram_args(c, wdt, W, N, K, g, Tb);
+  a.P = w.F; a.DB = w.DB; a.partials = w.partials;
+  a.bestV = w.bestV; a.bestA = w.bestA; a.bestB = w.bestB;
+  for (int i = 0; i < c->iters; ++i) {
+    const int64_t b = i % nb, bp = (i + nb - 1) % nb;
+    const int cur = i & 1;
+    hipEvent_t* e = (ntimed > 0 && i % every == 0) ? &ev[(size_t)(i / every) * 4] : nullptr;
+    // P = D·H; workgroup 0 settles the previous step's loss and best-loss decision
+    ArLossIn li{};
+    if (i > 0) {
+      li.partials = w.partials; li.nparts = nparts; li.inv_count = inv_count;
+      li.add = w.e2 + bp; li.loss_slot = losses ? losses + (i - 1) : nullptr;
+      li.best_loss = w.best_loss; li.flag = w.flag;
+    }
+    if (e && hipEventRecord(e[0], st) != hipSuccess) return cleanup(AR_ERR_HIP);
+    AR_TRY_C(ar_launch_gemm_f32out(w.DB, w.HB + b * q.hb, w.F, N, K, q.nkb3, 1.0f, li, st));
+    if (e && hipEventRecord(e[1], st) != hipSuccess) return cleanup(AR_ERR_HIP);
+    // update into the other half of the pair, copying the previous state to best
+    // first when its loss improved
+    a.Vc = w.V[cur]; a.Vn = w.V[1 - cur]; a.Ac = w.A[cur]; a.Bc = w.B[cur];
+    a.An = w.A[1 - cur]; a.Bn = w.B[1 - cur]; a.Cn = w.Cn + b * N * K;
+    a.flag_prev = i > 0 ? w.flag : nullptr;
+    if (e && hipEventRecord(e[2], st) != hipSuccess) return cleanup(AR_ERR_HIP);
+    AR_TRY_C(ar_launch_ste_gram(a, st));
+    if (e && hipEventRecord(e[3], st) != hipSuccess) return cleanup(AR_ERR_HIP);
+  }
+  if (c->iters > 0) {
+    // the last step's loss and snapshot (its state is still in its half of the pair)
+    const int last = (c->iters - 1) & 1;
+    ArLossIn li{};
+    li.partials = w.partials; li.nparts = nparts; li.inv_count = inv_count;
+    li.add = w.e2 + (c->iters - 1) % nb; li.loss_slot = losses ? losses + (c->iters - 1) : nullptr;
+    li.best_loss = w.best_loss; li.flag = w.flag;
+    AR_TRY_C(ar_launch_loss_reduce(li, st));
+    AR_TRY_C(ar_launch_gram_snapshot(w.flag, w.V[last], w.A[last], w.B[last], w.bestV, w.bestA,
+                                     w.bestB, N * K, N * Gn, st));
+  }
+  // restore the best state and quantize it (the initial state when iters = 0)
+  AR_TRY_C(ar_launch_fakequant(wdt, W, w.bestV, w.bestA, w.bestB, c->minmax_shrink, N, K, g, gr,
+                               wdt, Wq, 0, codes, scale, zp, st));
+  if (V_out && hipMemcpyAsync(V_out, w.bestV, (size_t)N * K * 4, hipMemcpyDeviceToDevice, st))
+    return cleanup(AR_ERR_HIP);
+  if (alpha_out &&
+      hipMemcpyAsync(alpha_out, w.bestA, (size_t)N * Gn * 4, hipMemcpyDeviceToDevice, st))
+    return cleanup(AR_ERR_HIP);
+  if (beta_out &&
+      hipMemcpyAsync(beta_out, w.bestB, (size_t)N * Gn * 4, hipMemcpyDeviceToDevice, st))
+    return cleanup(AR_ERR_HIP);
+  if (times) {
+    const int32_t sample = times->sample_every;
+    memset(times, 0, sizeof(*times));
+    times->sample_every = sample;
+    if (ntimed > 0) {
+      if (hipStreamSynchronize(st) != hipSuccess) return cleanup(AR_ERR_HIP);
+      for (int i = 0; i < ntimed; ++i) {
+        float ms[2];
+        for (int k = 0; k < 2; ++k)
+          if (hipEventElapsedTime(&ms[k], ev[(size_t)i * 4 + 2 * k], ev[(size_t)i * 4 + 2 * k + 1]) !=
+              hipSuccess)
+            return cleanup(AR_ERR_HIP);
+        times->fwd_gemm_ms += ms[0];
+        times->ste_update_ms += ms[1];
       }
       times->steps = ntimed;
     }

@@ -143,6 +143,13 @@ __device__ __forceinline__ QE quant_elem(float w, float v, const QP& p, const Gr
   return e;
 }
 
+// Sum over the 64 lanes of a wave (butterfly, fixed order; every lane gets it).
+__device__ __forceinline__ float wave_sum64(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
 // ---------------------------------------------------------------- loss reduction
 // Sum of n float32 partials in float64 by a block of 256 threads, in a fixed
 // order: thread t adds partials t, t+256, ... in turn, then a pairwise tree

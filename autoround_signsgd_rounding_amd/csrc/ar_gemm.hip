@@ -21,6 +21,7 @@
 #include "ar_blocked.h"
 #include "ar_device.h"
 #include "ar_launch.h"
+#include "ar_loss.h"
 
 namespace {
 
@@ -198,12 +199,6 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
 // main-loop steps; each lane turns its accumulators into R in place (8 bytes per
 // 4 tokens), then the workgroup streams the 128 KiB dYᵀ tile out with 16-byte
 // coalesced stores.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
-
 struct EpiFwdBf16 {
   static constexpr int kPrefetch = NSTAGE;     // 4 x 32 KiB = the whole target tile
   const uint16_t* yB;   // targets, blocked like dYᵀ (rows n, reduction t)
@@ -257,7 +252,7 @@ struct EpiFwdBf16 {
         }
       }
     }
-    sq = wave_sum(sq);
+    sq = wave_sum64(sq);
     const int wave = wi * 2 + wj;
     if (lane == 0) red[wave] = sq;
     __syncthreads();
@@ -315,7 +310,7 @@ struct EpiFwdF32 {
         }
       }
     }
-    sq = wave_sum(sq);
+    sq = wave_sum64(sq);
     const int wave = wi * 2 + wj;
     if (lane == 0) red[wave] = sq;
     __syncthreads();
@@ -323,25 +318,15 @@ struct EpiFwdF32 {
   }
 };
 
-// Loss of the step and the best-loss decision (see ArLossIn), reduced by the
-// gradient product's workgroup 0 while its first stages load.
+// Loss of the previous launch's partial sums (see ArLossIn), reduced by
+// workgroup 0 while its first stages load.
 __device__ __forceinline__ void loss_pre(const ArLossIn& L, uint8_t* extra) {
-  if (blockIdx.x != 0) return;
-  const double total = block_sum_f64(L.partials, L.nparts, reinterpret_cast<double*>(extra + 64));
-  if (threadIdx.x == 0) {
-    const float loss = (float)(total * L.inv_count);
-    if (L.loss_out) *L.loss_out = loss;
-    if (L.loss_slot) *L.loss_slot = loss;
-    int imp = 0;
-    if (L.best_loss) {
-      imp = loss < *L.best_loss;
-      if (imp) *L.best_loss = loss;
-    }
-    *L.flag = imp;
-  }
+  if (blockIdx.x != 0 || L.partials == nullptr) return;
+  loss_reduce_block(L, reinterpret_cast<double*>(extra + 64));
 }
 
-// Gradient epilogue: i = output feature n, j = input feature k; G = scale * acc.
+// float32 epilogue (weight gradient, Gram products): i = row of P, j = row of Q;
+// out[i, j] = scale * acc, rows i < N, columns j < K of a row-major [N, K].
 struct EpiWgrad {
   static constexpr int kPrefetch = 0;
   float* G;   // [N, K] row-major
@@ -395,15 +380,22 @@ ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void*
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 
+ar_status ar_launch_gemm_f32out(const uint16_t* P, const uint16_t* Q, float* out, int64_t rowsP,
+                                int64_t rowsQ, int64_t nkb, float scale, const ArLossIn& loss,
+                                hipStream_t st) {
+  GemmArgs a;
+  a.P = P; a.Q = Q;
+  a.nkb = (int)nkb;
+  a.tilesI = (int)arblk::row_tiles(rowsP);
+  a.tilesJ = (int)arblk::row_tiles(rowsQ);
+  EpiWgrad e{out, rowsP, rowsQ, scale, loss};
+  hipLaunchKernelGGL(k_gemm<EpiWgrad>, dim3(a.tilesI * a.tilesJ), dim3(NTHR), 0, st, a, e);
+  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
+}
+
 ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* G, int64_t N,
                                int64_t K, int64_t Tb, float scale, const ArLossIn& loss,
                                hipStream_t st) {
-  GemmArgs a;
-  a.P = dyB; a.Q = XTB;
-  a.nkb = (int)(arblk::row_tiles(Tb) * (BM / BK));
-  a.tilesI = (int)arblk::row_tiles(N);
-  a.tilesJ = (int)arblk::row_tiles(K);
-  EpiWgrad e{G, N, K, scale, loss};
-  hipLaunchKernelGGL(k_gemm<EpiWgrad>, dim3(a.tilesI * a.tilesJ), dim3(NTHR), 0, st, a, e);
-  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
+  return ar_launch_gemm_f32out(dyB, XTB, G, N, K, arblk::row_tiles(Tb) * (BM / BK), scale, loss,
+                               st);
 }

@@ -23,21 +23,30 @@ int ar_fwd_tiles(int64_t Tb, int64_t N);
 ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void* yB, int ydt,
                              uint16_t* dyB, float* partials, int64_t Tb, int64_t N, int64_t K,
                              hipStream_t st);
-// Loss of the step from the forward product's per-tile sums of R², reduced by
-// the gradient product's workgroup 0 (float64, fixed order) while its first
-// loads are in flight: loss = sum * inv_count, written to loss_out / loss_slot
-// (nullable); flag = (loss < *best_loss) with *best_loss lowered on
-// improvement, or flag = 0 when best_loss is NULL.
+// Loss of a step from per-workgroup partial sums of squared residuals, reduced
+// in float64 in a fixed order (ar_loss.h): total = sum(partials) + (*add when
+// add), *sum_out = total, loss = total * inv_count written to loss_out /
+// loss_slot, flag = (loss < *best_loss) with *best_loss lowered on
+// improvement (flag = 0 without best_loss). Every pointer but partials is
+// nullable; partials = NULL skips the reduction.
 struct ArLossIn {
   const float* partials;
   int nparts;
   double inv_count;     // 1 / (Tb * N)
+  const double* add;
+  double* sum_out;
   float* loss_out;
   float* loss_slot;
   float* best_loss;
   int* flag;
 };
-// G = scale * dYᵀ·X_b, row-major [N, K].
+// out[rowsP, rowsQ] (row-major float32) = scale * P·Qᵀ over nkb reduction
+// blocks (P rows rowsP, Q rows rowsQ, both blocked with nkb blocks per row
+// tile). Workgroup 0 reduces `loss` while its first stages load.
+ar_status ar_launch_gemm_f32out(const uint16_t* P, const uint16_t* Q, float* out, int64_t rowsP,
+                                int64_t rowsQ, int64_t nkb, float scale, const ArLossIn& loss,
+                                hipStream_t st);
+// G = scale * dYᵀ·X_b, row-major [N, K] (the weight-gradient product).
 ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* G, int64_t N,
                                int64_t K, int64_t Tb, float scale, const ArLossIn& loss,
                                hipStream_t st);
@@ -82,6 +91,52 @@ struct ArSteArgs {
 ar_status ar_launch_ste_update(const ArSteArgs& a, hipStream_t st);
 
 ar_status ar_launch_fill_f32(float* p, float v, int64_t n, hipStream_t st);
+
+// Gram-form step (ar_gram.hip). D operands are blocked with rows N and reduction
+// 3K ([D_hi | D_hi | D_lo]); H operands with rows K and reduction 3K
+// ([H_hi | H_lo | H_hi]).
+// Row-major src [R, C] (dtype src_dt, C % 8 == 0) into blocked dst (nkb blocks)
+// at reduction offset k_off; lo = 0: bf16(x), lo = 1: bf16(x - bf16(x)).
+ar_status ar_launch_place(const void* src, int src_dt, int64_t R, int64_t C, uint16_t* dst,
+                          int64_t nkb, int64_t k_off, int lo, hipStream_t st);
+// D operand of the state (V, A, B).
+ar_status ar_launch_gram_d(int wdt, const void* W, const float* V, const float* A, const float* B,
+                           int64_t N, int64_t K, int g, ArGrid gr, uint16_t* DB, hipStream_t st);
+struct ArGramArgs {
+  int wdt;
+  const void* W;
+  const float* Vc;       // state the product P was taken at
+  float* Vn;             // next state; on entry the previous state
+  const float* Ac;
+  const float* Bc;
+  float* An;
+  float* Bn;
+  const float* P;        // D·H [N, K]
+  const float* Cn;       // target correction [N, K]
+  int64_t N, K;
+  int g;
+  ArGrid gr;
+  float lr, mlr, clip_lo, clip_hi;
+  float scale;           // 2 / (Tb * N)
+  int apply;
+  const int* flag_prev;  // nullable: copy the previous state to best when set
+  float* bestV;
+  float* bestA;
+  float* bestB;
+  uint16_t* DB;          // next D operand
+  float* partials;       // ar_gram_partials() floats: per-workgroup sums of D·(P + 2·Cn)
+  float* gV;             // nullable gradient outputs
+  float* gA;
+  float* gB;
+};
+int64_t ar_gram_partials(int64_t N, int64_t K, int g);
+ar_status ar_launch_ste_gram(const ArGramArgs& a, hipStream_t st);
+// One-workgroup loss reduction (see ArLossIn).
+ar_status ar_launch_loss_reduce(const ArLossIn& L, hipStream_t st);
+// Copy (V, A, B) to (bestV, bestA, bestB) when *flag is set.
+ar_status ar_launch_gram_snapshot(const int* flag, const float* V, const float* A, const float* B,
+                                  float* bestV, float* bestA, float* bestB, int64_t nV, int64_t nG,
+                                  hipStream_t st);
 ar_status ar_launch_pack(int bits, const uint8_t* codes, const uint8_t* zp, int64_t N, int64_t K,
                          int64_t G, int32_t* qweight, int32_t* qzeros, hipStream_t st);
 ar_status ar_launch_unpack(int bits, const int32_t* qweight, const int32_t* qzeros, int64_t N,

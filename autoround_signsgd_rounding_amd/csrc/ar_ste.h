@@ -60,52 +60,70 @@ __device__ __forceinline__ void ste_accum(const float (&w)[8], const float (&v)[
   }
 }
 
-// One step for the elements of one chunk: dL/dV = G·s·m, optional snapshot of
-// the pre-update offset, V <- clamp(V - lr·sgn(dL/dV), -0.5, 0.5), and the bf16
-// fake-quant of the updated state for the next forward product.
-template <typename WT>
-__device__ __forceinline__ void ste_finish(const SteK<WT>& a, int64_t n, int64_t off, const float (&w)[8],
-                                           const float (&v)[8], const float (&g)[8], const QP& p,
-                                           const QP& pn, const Grid& gr, bool snap) {
-  float gv[8], vn[8], wq[8];
+// Per element of one chunk: dL/dV = G·s·m, V <- clamp(V - lr·sgn(dL/dV), -0.5,
+// 0.5) (unchanged when apply = 0), and the fake-quant Ŵ of the updated offset
+// under the updated group parameters pn.
+__device__ __forceinline__ void ste_chunk_update(const float (&w)[8], const float (&v)[8],
+                                                 const float (&g)[8], const QP& p, const QP& pn,
+                                                 const Grid& gr, float lr, int apply,
+                                                 float (&gv)[8], float (&vn)[8], float (&wq)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const QE e = quant_elem(w[i], v[i], p, gr);
     gv[i] = e.m ? g[i] * p.s : 0.0f;
     const float sg = e.m ? sgnf(g[i]) : 0.0f;
-    vn[i] = a.apply ? fminf(fmaxf(v[i] - a.lr * sg, -0.5f), 0.5f) : v[i];
+    vn[i] = apply ? fminf(fmaxf(v[i] - lr * sg, -0.5f), 0.5f) : v[i];
     wq[i] = quant_elem(w[i], vn[i], pn, gr).what;
   }
+}
+
+// One step for the elements of one chunk: the update above, an optional
+// snapshot of the pre-update offset, and the bf16 fake-quant of the updated
+// state for the next forward product.
+template <typename WT>
+__device__ __forceinline__ void ste_finish(const SteK<WT>& a, int64_t n, int64_t off, const float (&w)[8],
+                                           const float (&v)[8], const float (&g)[8], const QP& p,
+                                           const QP& pn, const Grid& gr, bool snap) {
+  float gv[8], vn[8], wq[8];
+  ste_chunk_update(w, v, g, p, pn, gr, a.lr, a.apply, gv, vn, wq);
   if (a.gV) store8(a.gV + off, gv);
   if (snap) store8(a.bestV + off, v);
   if (a.apply) store8(a.V + off, vn);
   if (a.Wq_next) store8(a.Wq_next + arblk::chunk_offset(n, off - n * a.K, a.wq_nkb), wq);
 }
 
-// Clip-factor gradients of one group (zero for a zero-range group), their
-// SignSGD step, and the per-group writes done by the group's first lane:
-// optional gradients, the pre-update snapshot, the updated factors.
+// Clip-factor gradients of one group from its straight-through sums (zero for
+// a zero-range group).
+__device__ __forceinline__ void clip_grads(const Grid& gr, const QP& p, float mn, float mx,
+                                           float al, float be, float A, float Bs, float& ga,
+                                           float& gb) {
+  ga = 0.0f;
+  gb = 0.0f;
+  if (p.zero) return;
+  if (gr.sym) {
+    const float damax = 2.0f * A / gr.maxq;
+    const bool to_alpha = fabsf(al * mn) > fabsf(be * mx);
+    ga = to_alpha ? damax * fabsf(mn) : 0.0f;
+    gb = to_alpha ? 0.0f : damax * fabsf(mx);
+  } else {
+    const float B = -p.s * Bs;
+    const float D = A + B * p.lo / (p.s * p.s);
+    const float dlo = -D / gr.maxq - B / p.s;
+    const float dhi = D / gr.maxq;
+    ga = (mn < 0.0f) ? dlo * mn : 0.0f;
+    gb = (mx > 0.0f) ? dhi * mx : 0.0f;
+  }
+}
+
+// The clip-factor gradients, their SignSGD step, and the per-group writes done
+// by the group's first lane: optional gradients, the pre-update snapshot, the
+// updated factors.
 template <typename WT>
 __device__ __forceinline__ void clip_update(const SteK<WT>& a, bool snap, int64_t gid, int lig,
                                             float mn, float mx, float al, float be, const QP& p,
                                             float A, float Bs, bool live, float& an, float& bn) {
-  const Grid gr = grid_of(a.gr);
-  float ga = 0.0f, gb = 0.0f;
-  if (!p.zero) {
-    if (gr.sym) {
-      const float damax = 2.0f * A / gr.maxq;
-      const bool to_alpha = fabsf(al * mn) > fabsf(be * mx);
-      ga = to_alpha ? damax * fabsf(mn) : 0.0f;
-      gb = to_alpha ? 0.0f : damax * fabsf(mx);
-    } else {
-      const float B = -p.s * Bs;
-      const float D = A + B * p.lo / (p.s * p.s);
-      const float dlo = -D / gr.maxq - B / p.s;
-      const float dhi = D / gr.maxq;
-      ga = (mn < 0.0f) ? dlo * mn : 0.0f;
-      gb = (mx > 0.0f) ? dhi * mx : 0.0f;
-    }
-  }
+  float ga, gb;
+  clip_grads(grid_of(a.gr), p, mn, mx, al, be, A, Bs, ga, gb);
   an = al;
   bn = be;
   if (a.apply) {

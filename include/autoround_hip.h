@@ -173,6 +173,48 @@ ar_status ar_tune_linear(const ar_config* cfg, int32_t wdt, const void* W, int64
                          float* beta_out, float* losses, void* ws, size_t ws_bytes,
                          ar_kernel_times* times, void* stream);
 
+/* ---- Gram form (same-input Linears) --------------------------------------
+   For one Linear the quantized and the reference outputs see the same tokens,
+   so the minibatch loss and its gradient depend on the tokens only through
+   H = Xbᵀ·Xb (the Hessian weight of the layer objective, ADMM-Q page "1. 문제
+   공식화"), Cn = (Xb·Wᵀ - Yb)ᵀ·Xb and e2 = |Xb·Wᵀ - Yb|²: with D = bf16(Ŵ) - W,
+     sum(R²) = Σ D∘(D·H) + 2·Σ D∘Cn + e2,   dL/dŴ = (2/(Tb·N))·(D·H + Cn).
+   This is the [LLMC] output-reconstruction loss with the residual kept
+   unrounded (the token form rounds dY to bf16), at 2·N·K·3K product FLOP per
+   step instead of 4·Tb·K·N: D·H runs as bf16 MFMA on a hi/lo split
+   (D_hi·H_hi + D_hi·H_lo + D_lo·H_hi, float32 accumulation). The statistics
+   are computed once per minibatch (three products of the minibatch's tokens).
+   Everything else (quantizer, straight-through fold, SignSGD, snapshot,
+   finalisation) is the token form's. */
+
+/* Bytes of device workspace for ar_tune_linear_gram (wdt: dtype of W). */
+ar_status ar_gram_workspace_size(const ar_config* cfg, int32_t wdt, int64_t N, int64_t K,
+                                 int32_t ydt, size_t* bytes);
+
+/* Bytes of device workspace for ar_tune_step_gram with a minibatch of Tb tokens. */
+ar_status ar_gram_step_workspace_size(const ar_config* cfg, int32_t wdt, int64_t N, int64_t K,
+                                      int64_t Tb, int32_t ydt, size_t* bytes);
+
+/* ar_tune_step in the Gram form: same arguments, state semantics and outputs
+   (loss_out = sum(R²)/(Tb·N) with R unrounded; gradients from D·H + Cn). The
+   minibatch's statistics are computed inside the call. ws:
+   ar_gram_step_workspace_size bytes. */
+ar_status ar_tune_step_gram(const ar_config* cfg, const ar_state* state, const uint16_t* Xb,
+                            const void* Yb, int32_t ydt, int64_t Tb, float* loss_out, float* gV,
+                            float* galpha, float* gbeta, int32_t apply_update, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* ar_tune_linear in the Gram form: same arguments and outputs. ws:
+   ar_gram_workspace_size bytes (the per-minibatch H and Cn live there: nb·(6·K·K
+   + 4·N·K) bytes for nb = nsamples/batch_samples minibatches). With times,
+   fwd_gemm_ms is the product D·H, ste_update_ms the update kernel and
+   wgrad_gemm_ms is 0. */
+ar_status ar_tune_linear_gram(const ar_config* cfg, int32_t wdt, const void* W, int64_t N,
+                              int64_t K, const uint16_t* X, const void* Y, int32_t ydt,
+                              uint8_t* codes, float* scale, uint8_t* zp, void* Wq, float* V_out,
+                              float* alpha_out, float* beta_out, float* losses, void* ws,
+                              size_t ws_bytes, ar_kernel_times* times, void* stream);
+
 /* Pack codes into 32-bit words ([SGL] pack_factor = Fraction(32, bits); GPTQ-style
    layout): code (n, k) occupies bits [k*bits, (k+1)*bits) of the bit string of
    column n, least significant bit first, so word w of column n is
