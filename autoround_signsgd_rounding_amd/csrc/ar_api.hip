@@ -606,7 +606,7 @@ ar_status ar_tune_step_gram(const ar_config* c, const ar_state* s, const uint16_
   AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(w.DB), 0.0f, q.db / 2, st));
   AR_TRY(ar_launch_gram_d(s->wdt, s->W, s->V, s->alpha, s->beta, N, K, g, grid_of(c), w.DB, st));
   ArLossIn none{};
-  AR_TRY(ar_launch_gemm_f32out(w.DB, w.HB, w.F, N, K, q.nkb3, 1.0f, none, st));
+  AR_TRY(ar_launch_gemm_gram(w.DB, w.HB, w.F, N, K, none, st));
   ArGramArgs a = gram_args(c, s->wdt, s->W, N, K, g, Tb);
   a.Vc = s->V; a.Vn = w.V[0]; a.Ac = s->alpha; a.Bc = s->beta; a.An = w.A[0]; a.Bn = w.B[0];
   a.P = w.F; a.Cn = w.Cn; a.apply = apply_update != 0; a.DB = w.DB; a.partials = w.partials;
@@ -715,7 +715,7 @@ ar_status ar_tune_linear_gram(const ar_config* c, int32_t wdt, const void* W, in
       li.best_loss = w.best_loss; li.flag = w.flag;
     }
     if (e && hipEventRecord(e[0], st) != hipSuccess) return cleanup(AR_ERR_HIP);
-    AR_TRY_C(ar_launch_gemm_f32out(w.DB, w.HB + b * q.hb, w.F, N, K, q.nkb3, 1.0f, li, st));
+    AR_TRY_C(ar_launch_gemm_gram(w.DB, w.HB + b * q.hb, w.F, N, K, li, st));
     if (e && hipEventRecord(e[1], st) != hipSuccess) return cleanup(AR_ERR_HIP);
     // update into the other half of the pair, copying the previous state to best
     // first when its loss improved

@@ -380,17 +380,34 @@ ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void*
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 
-ar_status ar_launch_gemm_f32out(const uint16_t* P, const uint16_t* Q, float* out, int64_t rowsP,
-                                int64_t rowsQ, int64_t nkb, float scale, const ArLossIn& loss,
-                                hipStream_t st) {
+// The Gram-form product D·H gets its own type so that profiles name it apart
+// from the weight-gradient product (same code).
+struct EpiGramP : EpiWgrad {};
+
+template <class Epi>
+static ar_status launch_f32out(const uint16_t* P, const uint16_t* Q, float* out, int64_t rowsP,
+                               int64_t rowsQ, int64_t nkb, float scale, const ArLossIn& loss,
+                               hipStream_t st) {
   GemmArgs a;
   a.P = P; a.Q = Q;
   a.nkb = (int)nkb;
   a.tilesI = (int)arblk::row_tiles(rowsP);
   a.tilesJ = (int)arblk::row_tiles(rowsQ);
-  EpiWgrad e{out, rowsP, rowsQ, scale, loss};
-  hipLaunchKernelGGL(k_gemm<EpiWgrad>, dim3(a.tilesI * a.tilesJ), dim3(NTHR), 0, st, a, e);
+  Epi e;
+  e.G = out; e.N = rowsP; e.K = rowsQ; e.scale = scale; e.loss = loss;
+  hipLaunchKernelGGL(k_gemm<Epi>, dim3(a.tilesI * a.tilesJ), dim3(NTHR), 0, st, a, e);
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
+}
+
+ar_status ar_launch_gemm_f32out(const uint16_t* P, const uint16_t* Q, float* out, int64_t rowsP,
+                                int64_t rowsQ, int64_t nkb, float scale, const ArLossIn& loss,
+                                hipStream_t st) {
+  return launch_f32out<EpiWgrad>(P, Q, out, rowsP, rowsQ, nkb, scale, loss, st);
+}
+
+ar_status ar_launch_gemm_gram(const uint16_t* DB, const uint16_t* HB, float* P, int64_t N,
+                              int64_t K, const ArLossIn& loss, hipStream_t st) {
+  return launch_f32out<EpiGramP>(DB, HB, P, N, K, arblk::k_blocks(3 * K), 1.0f, loss, st);
 }
 
 ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* G, int64_t N,

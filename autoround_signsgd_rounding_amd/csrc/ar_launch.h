@@ -46,6 +46,10 @@ struct ArLossIn {
 ar_status ar_launch_gemm_f32out(const uint16_t* P, const uint16_t* Q, float* out, int64_t rowsP,
                                 int64_t rowsQ, int64_t nkb, float scale, const ArLossIn& loss,
                                 hipStream_t st);
+// P = D·H, row-major [N, K]: DB rows N and HB rows K, both with k_blocks(3K)
+// reduction blocks (the Gram-form product).
+ar_status ar_launch_gemm_gram(const uint16_t* DB, const uint16_t* HB, float* P, int64_t N,
+                              int64_t K, const ArLossIn& loss, hipStream_t st);
 // G = scale * dYᵀ·X_b, row-major [N, K] (the weight-gradient product).
 ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* G, int64_t N,
                                int64_t K, int64_t Tb, float scale, const ArLossIn& loss,

@@ -12,6 +12,8 @@ average duration measured by HIP events on the launch stream during the timed
 steps; `cpu_baseline` is the CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--workload llama7b_q_proj]
+
+detail.gram reports the same job in the Gram form (ar_tune_linear_gram).
 """
 import argparse
 import json
@@ -90,6 +92,53 @@ def _cpu_baseline(case, Yd, w, steps=2):
             "host_cpus": os.cpu_count(), "host": platform.processor() or platform.machine()}
 
 
+def _gram_run(ar, torch, W, X, Y, cfg, w, args):
+    """The same job in the Gram form (ar_tune_linear_gram + ar_pack): per-minibatch
+    statistics staged inside the call, then one D·H product (2·N·K·3K FLOP on a
+    hi/lo bf16 split) and one update kernel per iteration."""
+    ws = torch.empty(ar.gram_workspace_size(cfg, ar.AR_BF16 if W.dtype == torch.bfloat16
+                                            else ar.AR_F32, w.N, w.K,
+                                            ar.AR_BF16 if Y.dtype == torch.bfloat16
+                                            else ar.AR_F32), dtype=torch.uint8, device=W.device)
+    recs = []
+
+    def step(keep):
+        out = ar.tune_linear(W, X, Y, cfg, want_state=False, timed=True, time_every=TIME_EVERY,
+                             workspace=ws, gram=True)
+        ar.pack(out.codes, out.zp, w.bits)
+        if keep:
+            recs.append(out)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    iters_total = w.iters * args.steps
+    timed = sum(r.times.steps for r in recs)
+    prod_ms = sum(r.times.fwd_gemm_ms for r in recs) / timed
+    upd_ms = sum(r.times.ste_update_ms for r in recs) / timed
+    prod_flop = 2.0 * w.N * w.K * 3 * w.K
+    achieved = prod_flop / (prod_ms * 1e-3) / 1e12
+    del ws
+    torch.cuda.empty_cache()
+    return {
+        "value": round(iters_total / el, 3), "unit": "iters/s",
+        "ms_per_step": round(el / args.steps * 1e3, 3),
+        "ms_per_iter": round(el / iters_total * 1e3, 4),
+        "kernel_ms_per_iter": {"gram_product": round(prod_ms, 4), "update": round(upd_ms, 4)},
+        "roofline": {"kernel": "gram_product", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4)},
+        "first_loss": float(recs[-1].losses[0]), "best_loss": float(recs[-1].losses.min()),
+        "note": "same loss with the residual unrounded; per-minibatch H, Cn, e2 staged "
+                "inside each timed call",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +146,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="llama7b_q_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gram", action="store_true",
+                    help="skip the Gram-form run reported under detail.gram")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -223,6 +274,8 @@ def main():
             "input_gen_s": round(t_gen, 1),
         },
     }
+    if not args.no_gram:
+        line["detail"]["gram"] = _gram_run(ar, torch, W, X, Y, cfg, w, args)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = _cpu_baseline(case, Y, w)
     print(json.dumps(line), flush=True)

@@ -5,7 +5,8 @@ Calls only ``oracle`` and ``synth`` (never the HIP library). Runs the full
 fixed sample of output rows, the final codes / scales / zero-points / clip
 factors, plus the whole loss trajectory and the best step.
 
-    python tests/golden/make_golden.py llama7b_q_proj      # ~15 min on 8 cores
+    python tests/golden/make_golden.py llama7b_q_proj          # ~15 min on 8 cores
+    python tests/golden/make_golden.py llama7b_q_proj --gram   # the oracle's Gram mode
 """
 import os
 import sys
@@ -27,7 +28,7 @@ def sample_rows(N):
     return np.sort(np.random.default_rng(ROW_SEED).choice(N, size=min(N_ROWS, N), replace=False))
 
 
-def main(name):
+def main(name, gram=False):
     w = synth.WORKLOADS[name]
     t0 = time.time()
     case = synth.make_workload_case(w)
@@ -48,10 +49,11 @@ def main(name):
     def on_step(i, r):
         print(f"step {i} loss {r.loss:.9e} t={time.time() - t0:.0f}s", flush=True)
 
-    res = O.tune_linear(case.W, minibatch, nb, cfg, on_step=on_step)
+    res = O.tune_linear(case.W, minibatch, nb, cfg, on_step=on_step, gram=gram)
     rtn_codes, _, _, _ = O.rtn_quant(case.W, cfg)
     rows = sample_rows(w.N)
-    out = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"tune_{name}.npz")
+    tag = "tune_gram_" if gram else "tune_"
+    out = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"{tag}{name}.npz")
     np.savez_compressed(
         out, rows=rows, losses=np.array(res.losses, np.float64),
         best_step=np.int64(res.best_step), best_loss=np.float64(res.best_loss),
@@ -63,4 +65,5 @@ def main(name):
 
 
 if __name__ == "__main__":
-    main(sys.argv[1] if len(sys.argv) > 1 else "llama7b_q_proj")
+    args = [a for a in sys.argv[1:] if not a.startswith("--")]
+    main(args[0] if args else "llama7b_q_proj", gram="--gram" in sys.argv)
