@@ -38,6 +38,7 @@ Readings where the pages are silent or garbled are listed in the design doc.
 from __future__ import annotations
 
 import dataclasses
+import re
 import math
 
 import numpy as np
@@ -63,6 +64,8 @@ class Config:
     minmax_shrink: float = 1.0     # initial alpha = beta
     clip_lo: float = 0.5           # alpha/beta clamp range
     clip_hi: float = 1.0
+    init: str = "minmax"           # initial scale: "minmax" or "mse"
+    mse_grid: int = 100            # shrink grid steps per unit for init = "mse"
 
     @property
     def maxq(self) -> int:
@@ -176,6 +179,66 @@ def fake_quant(W, V, qp: QParams, bits: int, group_size: int) -> FakeQuant:
     m = (c >= 0) & (c <= maxq)
     what = s_e * (q - zp_e)
     return FakeQuant(t=t, q=q, m=m, what=what, s_e=s_e, zp_e=zp_e)
+
+
+# ------------------------------------------------------------------ initial scale
+def mse_grid_points(cfg: Config) -> np.ndarray:
+    """Shrink candidates of the MSE initial scale, largest first: the values
+    p_j = float32(1 - j/mse_grid) (formed in float64, rounded once), j = 0, 1,
+    ..., that lie in [clip_lo, clip_hi] (float32 comparisons), so every
+    candidate is a valid clip factor. ValueError when there is none."""
+    lo, hi = F32(cfg.clip_lo), F32(cfg.clip_hi)
+    if cfg.mse_grid < 1:
+        raise ValueError("mse_grid must be >= 1")
+    pts = []
+    j = 0
+    while True:
+        p = F32(1.0 - j / cfg.mse_grid)
+        if p < lo:
+            break
+        if p <= hi:
+            pts.append(p)
+        j += 1
+    if not pts:
+        raise ValueError("no MSE grid point inside [clip_lo, clip_hi]")
+    return np.array(pts, F32)
+
+
+def mse_shrink(W, cfg: Config) -> np.ndarray:
+    """MSE initial scale ([LLMC] tuning loop: initial scale / zero-point by
+    "Min-Max or MSE"): per group, the shrink p of the grid whose round-to-
+    nearest quantization (V = 0, alpha = beta = p) has the smallest sum of
+    squared weight errors. Errors are formed in float32 (w - Ŵ, squared) and
+    summed in float64; ties go to the earlier, larger p. Returns p [N, G]."""
+    W = np.asarray(W, F32)
+    N, K = W.shape
+    g = cfg.g(K)
+    Gn = K // g
+    wmin, wmax = group_minmax(W, cfg.group_size)
+    V0 = np.zeros((N, K), F32)
+    errs = []
+    pts = mse_grid_points(cfg)
+    for p in pts:
+        a = np.full(wmin.shape, p, F32)
+        qp = qparams(wmin, wmax, a, a, cfg.bits, cfg.sym)
+        fq = fake_quant(W, V0, qp, cfg.bits, cfg.group_size)
+        d = (W - fq.what).astype(F32)
+        e = (d * d).astype(F32)
+        errs.append(e.astype(F64).reshape(N, Gn, g).sum(axis=2))
+    best = np.argmin(np.stack(errs), axis=0)          # first minimum on ties
+    return pts[best]
+
+
+def init_clip(W, cfg: Config):
+    """Initial clip factors (alpha, beta) [N, G]: minmax_shrink everywhere
+    (init = "minmax"), or the MSE shrink of each group (init = "mse")."""
+    N, K = np.shape(W)
+    Gn = K // cfg.g(K)
+    if cfg.init == "mse":
+        p = mse_shrink(W, cfg)
+        return p.copy(), p.copy()
+    a = np.full((N, Gn), F32(cfg.minmax_shrink), F32)
+    return a, a.copy()
 
 
 # ------------------------------------------------------------------ S4-S7
@@ -367,12 +430,12 @@ def quantize_state(W, V, alpha, beta, wmin, wmax, cfg: Config):
 
 
 def rtn_quant(W, cfg: Config):
-    """Round-to-nearest: V = 0 and alpha = beta = minmax_shrink ([LLMC] RTN
+    """Round-to-nearest: V = 0 and the initial clip factors ([LLMC] RTN
     equation; [INTEL] section 4: zero iterations give RTN)."""
     N, K = W.shape
     wmin, wmax = group_minmax(W, cfg.group_size)
-    a = np.full(wmin.shape, F32(cfg.minmax_shrink), F32)
-    return quantize_state(W, np.zeros((N, K), F32), a, a.copy(), wmin, wmax, cfg)
+    a, b = init_clip(W, cfg)
+    return quantize_state(W, np.zeros((N, K), F32), a, b, wmin, wmax, cfg)
 
 
 def tune_linear(W, minibatch, nb: int, cfg: Config, *, amp: bool = True,
@@ -391,8 +454,7 @@ def tune_linear(W, minibatch, nb: int, cfg: Config, *, amp: bool = True,
     stats = {}
     wmin, wmax = group_minmax(W, cfg.group_size)
     V = np.zeros((N, K), F32)
-    alpha = np.full(wmin.shape, F32(cfg.minmax_shrink), F32)
-    beta = alpha.copy()
+    alpha, beta = init_clip(W, cfg)
     best = (V.copy(), alpha.copy(), beta.copy())
     best_loss, best_step = math.inf, -1
     losses = []
@@ -495,3 +557,59 @@ def brute_force_rounding(W, X, Y, qp: QParams, bits: int, group_size: int):
                 best_val[n] = val
                 best_codes[n] = c.astype(np.uint8)
     return best_val, best_codes
+
+
+# ------------------------------------------------------------------ per-layer config
+REGEX_SPECIAL_CHARS = set("*+?^$()[]{}|\\")
+
+
+def resolve_layer_config(rules, defaults, quantized: bool, name: str):
+    """(bits, group_size, sym) of one layer from per-layer rules ([SGL]
+    "2. 레이어별 개별 설정" and "3. 정규식 기반 레이어 매칭"). ``rules`` is an
+    ordered list of (key, cfg dict with optional "bits", "group_size", "sym").
+      - no rules: the defaults, or (16, -1, True) for a layer outside the
+        quantized set;
+      - an exact key match: its values, the missing ones from the defaults
+        (from (16, -1, True) outside the quantized set);
+      - else the first key that contains a regular-expression special
+        character and fully matches the name: its values, missing ones from the
+        defaults; keys that do not compile are skipped;
+      - else as with no rules.
+    16 bits means "leave unquantized"."""
+    bits, gs, sym = defaults
+    unq = (16, -1, True)
+    if not rules:
+        return tuple(defaults) if quantized else unq
+    for key, cfg in rules:
+        if key == name:
+            return (cfg.get("bits", bits if quantized else 16),
+                    cfg.get("group_size", gs if quantized else -1),
+                    cfg.get("sym", sym if quantized else True))
+    for key, cfg in rules:
+        if not any(c in REGEX_SPECIAL_CHARS for c in key):
+            continue
+        try:
+            if re.fullmatch(key, name):
+                return (cfg.get("bits", bits), cfg.get("group_size", gs), cfg.get("sym", sym))
+        except re.error:
+            continue
+    return tuple(defaults) if quantized else unq
+
+
+def resolve_fused_config(rules, defaults, quantized: bool, layer_name: str, sub_names=None):
+    """Config of a fused layer ([SGL] "4. FusedMoE와 Fused QKV 처리"): all of its
+    sub-layers must resolve to the same config, else ValueError. With
+    ``sub_names`` (a fused q/k/v-style layer) those names are resolved; without
+    (a fused expert layer) the sub-layers are the rule keys that start with the
+    layer's name, and a layer with no such key resolves as itself."""
+    if sub_names is None:
+        names = [k for k, _ in rules if k.startswith(layer_name)]
+        if not names:
+            return resolve_layer_config(rules, defaults, quantized, layer_name)
+    else:
+        names = list(sub_names)
+    cfgs = [resolve_layer_config(rules, defaults, quantized, n) for n in names]
+    if len(set(cfgs)) != 1:
+        raise ValueError(f"fused layer {layer_name!r}: sub-layer configs differ: {cfgs}")
+    return cfgs[0]
+

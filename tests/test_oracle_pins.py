@@ -430,3 +430,147 @@ def test_pack_matches_bigint_and_roundtrips(bits):
     c2, z2 = O.unpack(qw, qz, bits, N, K)
     np.testing.assert_array_equal(c2, codes)
     np.testing.assert_array_equal(z2, zp)
+
+
+# ------------------------------------------------------------------ initial scale (MSE)
+def _mse_err(W, p, cfg):
+    """Squared RTN error of every group at shrink p (alpha = beta = p)."""
+    N, K = W.shape
+    g = cfg.g(K)
+    wmin, wmax = O.group_minmax(W, cfg.group_size)
+    a = np.full(wmin.shape, F32(p))
+    qp = O.qparams(wmin, wmax, a, a, cfg.bits, cfg.sym)
+    fq = O.fake_quant(W, np.zeros_like(W), qp, cfg.bits, cfg.group_size)
+    d = (W - fq.what).astype(np.float64)
+    return (d * d).reshape(N, K // g, g).sum(axis=2)
+
+
+def test_mse_grid_points():
+    pts = O.mse_grid_points(O.Config())
+    assert len(pts) == 51 and pts[0] == 1.0 and pts[-1] == F32(0.5)
+    assert np.all(np.diff(pts) < 0)
+    assert len(O.mse_grid_points(O.Config(clip_lo=0.8, mse_grid=20))) == 5
+    np.testing.assert_array_equal(O.mse_grid_points(O.Config(clip_lo=0.7, clip_hi=0.9,
+                                                             mse_grid=10)),
+                                  np.array([0.9, 0.8, 0.7], F32))
+    with pytest.raises(ValueError):
+        O.mse_grid_points(O.Config(clip_lo=0.91, clip_hi=0.99, mse_grid=10))
+
+
+@pytest.mark.parametrize("sym,bits", [(False, 2), (False, 4), (True, 3)])
+def test_mse_shrink_never_worse_than_minmax(sym, bits):
+    rng = np.random.default_rng(40 + bits)
+    W = (rng.standard_normal((24, 64)) * 0.02).astype(F32)
+    W[:, 5] *= 12.0                                         # an outlier column
+    cfg = O.Config(bits=bits, group_size=16, sym=sym, init="mse")
+    p = O.mse_shrink(W, cfg)
+    assert p.min() >= F32(0.5) and p.max() <= 1.0
+    e_best = np.minimum.reduce([_mse_err(W, q, cfg) for q in O.mse_grid_points(cfg)])
+    np.testing.assert_allclose(np.array([[_mse_err(W[n:n + 1], p[n, j], cfg)[0, j]
+                                          for j in range(p.shape[1])] for n in range(24)]),
+                               e_best, rtol=1e-12)
+    assert np.all(e_best <= _mse_err(W, 1.0, cfg))
+    assert (p < 1.0).any()                                  # outlier groups get clipped
+
+
+def test_mse_shrink_keeps_an_exact_grid():
+    """Values exactly on the min-max grid quantize with zero error at p = 1, so
+    p = 1 (the first candidate) is kept."""
+    s, zp = F32(0.125), 1
+    row = (s * (np.arange(4, dtype=F32) - zp)).astype(F32)  # [-0.125, 0, 0.125, 0.25], 2 bits
+    W = np.tile(row, (3, 2))
+    p = O.mse_shrink(W, O.Config(bits=2, group_size=4, init="mse"))
+    np.testing.assert_array_equal(p, np.ones_like(p))
+
+
+def test_mse_shrink_single_outlier_prefers_clipping():
+    """Seven small values and one large one at 2 bits: shrinking the range
+    trades a larger error on the outlier for a finer grid on the rest."""
+    W = np.array([[0.011, -0.02, 0.017, -0.005, 0.013, -0.019, 0.008, 0.2]], F32)
+    cfg = O.Config(bits=2, group_size=8, init="mse")
+    p = O.mse_shrink(W, cfg)
+    assert p[0, 0] < 1.0
+    assert _mse_err(W, p[0, 0], cfg)[0, 0] < _mse_err(W, 1.0, cfg)[0, 0]
+
+
+def test_mse_shrink_power_of_two_scaling():
+    rng = np.random.default_rng(44)
+    W = (rng.standard_normal((16, 128)) * 0.03).astype(F32)
+    cfg = O.Config(bits=3, group_size=32, init="mse")
+    np.testing.assert_array_equal(O.mse_shrink(W, cfg), O.mse_shrink(W * F32(8.0), cfg))
+
+
+def test_mse_init_feeds_rtn_and_loop():
+    W, X, Y = _full_batch_problem()
+    cfg = _cfg(bits=2, group_size=16, iters=0)
+    cfg.init = "mse"
+    a, b = O.init_clip(W, cfg)
+    np.testing.assert_array_equal(a, O.mse_shrink(W, cfg))
+    codes, s, zp, what = O.rtn_quant(W, cfg)
+    r = O.tune_linear(W, lambda i: (X, Y), 1, cfg)
+    np.testing.assert_array_equal(r.codes, codes)
+    np.testing.assert_array_equal(r.alpha, a)
+    cfg_mm = _cfg(bits=2, group_size=16, iters=0)
+    e_mse = float(((W - what) ** 2).sum())
+    e_mm = float(((W - O.rtn_quant(W, cfg_mm)[3]) ** 2).sum())
+    assert e_mse <= e_mm
+
+
+# ------------------------------------------------------------------ per-layer config
+DEF = (4, 128, False)
+
+
+def test_layer_config_without_rules():
+    assert O.resolve_layer_config([], DEF, True, "model.layers.0.mlp.up_proj") == (4, 128, False)
+    assert O.resolve_layer_config([], DEF, False, "lm_head") == (16, -1, True)
+
+
+def test_layer_config_exact_then_regex():
+    rules = [
+        (r"model\.layers\.\d+\.mlp\..*", {"bits": 8}),
+        ("model.layers.0.mlp.down_proj", {"bits": 2, "group_size": 64}),
+        (r"model\.layers\.1\..*", {"bits": 3, "sym": True}),
+        ("lm_head", {"bits": 16}),
+    ]
+    # an exact key wins over an earlier pattern
+    assert O.resolve_layer_config(rules, DEF, True, "model.layers.0.mlp.down_proj") == (2, 64, False)
+    # the first pattern that fully matches wins
+    assert O.resolve_layer_config(rules, DEF, True, "model.layers.1.mlp.up_proj") == (8, 128, False)
+    assert O.resolve_layer_config(rules, DEF, True, "model.layers.1.self_attn.q_proj") == (3, 128, True)
+    # full match only
+    assert O.resolve_layer_config(rules, DEF, True, "x.model.layers.1.self_attn.q_proj") == DEF
+    assert O.resolve_layer_config(rules, DEF, True, "lm_head") == (16, 128, False)
+    assert O.resolve_layer_config(rules, DEF, True, "model.layers.2.self_attn.o_proj") == DEF
+
+
+def test_layer_config_plain_keys_are_not_patterns():
+    """'.' is not in the special set: a dotted key is only an exact name."""
+    rules = [("model.layers.0.mlp", {"bits": 8})]
+    assert O.resolve_layer_config(rules, DEF, True, "modelXlayersX0Xmlp") == DEF
+    assert O.resolve_layer_config(rules, DEF, True, "model.layers.0.mlp") == (8, 128, False)
+
+
+def test_layer_config_bad_pattern_skipped():
+    rules = [("layers.(", {"bits": 2}), (r"layers\.\d", {"bits": 3})]
+    assert O.resolve_layer_config(rules, DEF, True, "layers.7") == (3, 128, False)
+
+
+def test_layer_config_outside_quantized_set():
+    """Exact keys fill missing fields from (16, -1, True) outside the quantized
+    set; pattern matches fill them from the defaults."""
+    rules = [("lm_head", {"group_size": 32}), (r"embed.*", {"sym": True})]
+    assert O.resolve_layer_config(rules, DEF, False, "lm_head") == (16, 32, True)
+    assert O.resolve_layer_config(rules, DEF, False, "embed_tokens") == (4, 128, True)
+    assert O.resolve_layer_config(rules, DEF, False, "norm") == (16, -1, True)
+
+
+def test_fused_configs():
+    rules = [("m.q_proj", {"bits": 8}), ("m.k_proj", {"bits": 8}), ("m.v_proj", {"bits": 4}),
+             ("e.experts.0.w1", {"bits": 3}), ("e.experts.1.w1", {"bits": 3})]
+    with pytest.raises(ValueError):
+        O.resolve_fused_config(rules, DEF, True, "m.qkv_proj", ["m.q_proj", "m.k_proj", "m.v_proj"])
+    assert O.resolve_fused_config(rules, DEF, True, "m.qk", ["m.q_proj", "m.k_proj"]) == (8, 128, False)
+    assert O.resolve_fused_config(rules, DEF, True, "e.experts") == (3, 128, False)
+    assert O.resolve_fused_config(rules, DEF, True, "f.experts") == DEF
+    with pytest.raises(ValueError):
+        O.resolve_fused_config(rules + [("e.experts.2.w1", {"bits": 2})], DEF, True, "e.experts")
