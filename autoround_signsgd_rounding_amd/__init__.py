@@ -27,7 +27,7 @@ EXPORTS = (
     "ar_config_default", "ar_status_string", "ar_workspace_size", "ar_step_workspace_size",
     "ar_rtn_quant", "ar_fakequant_fwd", "ar_tune_step", "ar_tune_linear", "ar_pack", "ar_unpack",
     "ar_gram_workspace_size", "ar_gram_step_workspace_size", "ar_tune_step_gram",
-    "ar_tune_linear_gram",
+    "ar_tune_linear_gram", "ar_init_clip", "ar_resolve_layer_config", "ar_resolve_fused_config",
 )
 
 
@@ -38,7 +38,8 @@ class ArConfig(ctypes.Structure):
         ("batch_samples", ctypes.c_int32), ("iters", ctypes.c_int32),
         ("lr", ctypes.c_float), ("minmax_lr", ctypes.c_float),
         ("minmax_shrink", ctypes.c_float), ("clip_lo", ctypes.c_float),
-        ("clip_hi", ctypes.c_float),
+        ("clip_hi", ctypes.c_float), ("init_scale", ctypes.c_int32),
+        ("mse_grid", ctypes.c_int32),
     ]
 
 
@@ -61,6 +62,16 @@ class ArKernelTimes(ctypes.Structure):
     ]
 
 
+class ArLayerRule(ctypes.Structure):
+    _fields_ = [("key", ctypes.c_char_p), ("bits", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("sym", ctypes.c_int32)]
+
+
+class ArLayerQConfig(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("sym", ctypes.c_int32)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -74,6 +85,7 @@ def _load():
         "ar_workspace_size": [cfgp, i64, i64, i32, ctypes.POINTER(sz)],
         "ar_step_workspace_size": [cfgp, i64, i64, i64, i32, ctypes.POINTER(sz)],
         "ar_rtn_quant": [cfgp, i32, vp, i64, i64, vp, vp, vp, vp, vp],
+        "ar_init_clip": [cfgp, i32, vp, i64, i64, vp, vp, vp],
         "ar_fakequant_fwd": [cfgp, i32, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp],
         "ar_tune_step": [cfgp, ctypes.POINTER(ArState), vp, vp, i32, i64, vp, vp, vp, vp, i32,
                          vp, sz, vp],
@@ -85,6 +97,13 @@ def _load():
                               i32, vp, sz, vp],
         "ar_tune_linear_gram": [cfgp, i32, vp, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp,
                                 vp, vp, sz, ctypes.POINTER(ArKernelTimes), vp],
+        "ar_resolve_layer_config": [ctypes.POINTER(ArLayerRule), i32,
+                                    ctypes.POINTER(ArLayerQConfig), i32, ctypes.c_char_p,
+                                    ctypes.POINTER(ArLayerQConfig)],
+        "ar_resolve_fused_config": [ctypes.POINTER(ArLayerRule), i32,
+                                    ctypes.POINTER(ArLayerQConfig), i32, ctypes.c_char_p,
+                                    ctypes.POINTER(ctypes.c_char_p), i32,
+                                    ctypes.POINTER(ArLayerQConfig)],
         "ar_pack": [i32, vp, vp, i64, i64, i64, vp, vp, vp],
         "ar_unpack": [i32, vp, vp, i64, i64, i64, vp, vp, vp],
     }
@@ -127,12 +146,17 @@ class Config:
     minmax_shrink: float = 1.0
     clip_lo: float = 0.5
     clip_hi: float = 1.0
+    init: str = "minmax"       # initial scale: "minmax" or "mse"
+    mse_grid: int = 100
 
     def c(self) -> ArConfig:
+        if self.init not in ("minmax", "mse"):
+            raise ValueError(f"init must be 'minmax' or 'mse', not {self.init!r}")
         return ArConfig(self.bits, self.group_size, int(self.sym), self.nsamples, self.seqlen,
                         self.batch_samples, self.iters, self.lr,
                         -1.0 if self.minmax_lr is None else self.minmax_lr,
-                        self.minmax_shrink, self.clip_lo, self.clip_hi)
+                        self.minmax_shrink, self.clip_lo, self.clip_hi,
+                        1 if self.init == "mse" else 0, self.mse_grid)
 
     def G(self, K: int) -> int:
         return 1 if self.group_size == -1 else K // self.group_size
@@ -202,6 +226,20 @@ def gram_step_workspace_size(cfg: Config, wdt: int, N: int, K: int, Tb: int, ydt
     _check(lib.ar_gram_step_workspace_size(ctypes.byref(cc), wdt, N, K, Tb, ydtype,
                                            ctypes.byref(out)), "ar_gram_step_workspace_size")
     return out.value
+
+
+def init_clip(W, cfg: Config, stream=None):
+    """Initial clip factors (alpha, beta) [N, G] float32 (Min-Max shrink or MSE search)."""
+    torch = _torch()
+    _dev(W)
+    N, K = W.shape
+    G = cfg.G(K)
+    alpha = torch.empty((N, G), dtype=torch.float32, device=W.device)
+    beta = torch.empty_like(alpha)
+    cc = cfg.c()
+    _check(lib.ar_init_clip(ctypes.byref(cc), _dt(W), _ptr(W), N, K, _ptr(alpha), _ptr(beta),
+                            _stream(stream)), "ar_init_clip")
+    return alpha, beta
 
 
 def rtn_quant(W, cfg: Config, stream=None, want_wq: bool = True):
@@ -348,3 +386,40 @@ def unpack(qweight, qzeros, bits: int, N: int, K: int, G: int, stream=None):
     _check(lib.ar_unpack(bits, _ptr(qweight), _ptr(qzeros), N, K, G, _ptr(codes), _ptr(zp),
                          _stream(stream)), "ar_unpack")
     return codes, zp
+
+
+# ------------------------------------------------------------------ per-layer config
+def _rules(rules):
+    """[(key, {"bits", "group_size", "sym"} subset), ...] -> ctypes array."""
+    arr = (ArLayerRule * max(len(rules), 1))()
+    for i, (key, cfg) in enumerate(rules):
+        arr[i] = ArLayerRule(key.encode(), int(cfg.get("bits", -1)),
+                             int(cfg.get("group_size", 0)),
+                             int(cfg["sym"]) if "sym" in cfg else -1)
+    return arr
+
+
+def resolve_layer_config(rules, defaults, quantized: bool, name: str):
+    """(bits, group_size, sym) of one layer (ar_resolve_layer_config)."""
+    arr = _rules(rules)
+    d = ArLayerQConfig(*[int(x) for x in defaults])
+    out = ArLayerQConfig()
+    _check(lib.ar_resolve_layer_config(arr, len(rules), ctypes.byref(d), int(quantized),
+                                       name.encode(), ctypes.byref(out)),
+           "ar_resolve_layer_config")
+    return out.bits, out.group_size, bool(out.sym)
+
+
+def resolve_fused_config(rules, defaults, quantized: bool, layer_name: str, sub_names=None):
+    """Config of a fused layer (ar_resolve_fused_config); ArError when its
+    sub-layers disagree."""
+    arr = _rules(rules)
+    d = ArLayerQConfig(*[int(x) for x in defaults])
+    out = ArLayerQConfig()
+    subs = list(sub_names or [])
+    names = (ctypes.c_char_p * max(len(subs), 1))(*[n.encode() for n in subs])
+    _check(lib.ar_resolve_fused_config(arr, len(rules), ctypes.byref(d), int(quantized),
+                                       layer_name.encode(), names, len(subs),
+                                       ctypes.byref(out)), "ar_resolve_fused_config")
+    return out.bits, out.group_size, bool(out.sym)
+

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libautoround_hip.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["ar_api.hip", "ar_gemm.hip", "ar_gram.hip", "ar_quant.hip"]
+SOURCES = ["ar_api.hip", "ar_gemm.hip", "ar_gram.hip", "ar_quant.hip", "ar_layers.cpp"]
 
 # -ffp-contract=off: the quantizer's float32 steps must round exactly as
 # written (no fused multiply-adds). Packed-fp32 instructions are disabled.
@@ -28,7 +28,7 @@ FLAGS = [
 
 
 def _compile(src):
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

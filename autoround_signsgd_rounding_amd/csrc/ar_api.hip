@@ -26,6 +26,30 @@ ArGrid grid_of(const ar_config* c) {
   return g;
 }
 
+// Candidate range of the MSE initial scale: j0..j1 with p_j = float32(1 - j/grid)
+// inside [clip_lo, clip_hi]. False when there is none.
+bool mse_range(const ar_config* c, int* j0, int* j1) {
+  *j0 = -1;
+  *j1 = -1;
+  for (int j = 0;; ++j) {
+    const float p = (float)(1.0 - (double)j / (double)c->mse_grid);
+    if (p < c->clip_lo) break;
+    if (p <= c->clip_hi) {
+      if (*j0 < 0) *j0 = j;
+      *j1 = j;
+    }
+  }
+  return *j0 >= 0;
+}
+
+ArInit init_of(const ar_config* c) {
+  ArInit in{};
+  in.shrink = c->minmax_shrink;
+  in.grid = c->mse_grid;
+  in.mse = c->init_scale == 1 && mse_range(c, &in.j0, &in.j1);
+  return in;
+}
+
 // bits / group / sym / shape checks shared by every quantizing entry point.
 // *g = group size in elements (0 when N*K == 0).
 ar_status check_quant(const ar_config* c, int64_t N, int64_t K, int* g) {
@@ -34,6 +58,14 @@ ar_status check_quant(const ar_config* c, int64_t N, int64_t K, int* g) {
   if (c->sym != 0 && c->sym != 1) return AR_ERR_INVALID_ARG;
   if (c->group_size != -1 && c->group_size <= 0) return AR_ERR_INVALID_ARG;
   if (!finite(c->minmax_shrink) || c->minmax_shrink <= 0.0f) return AR_ERR_INVALID_ARG;
+  if (c->init_scale != 0 && c->init_scale != 1) return AR_ERR_INVALID_ARG;
+  if (c->init_scale == 1) {
+    int j0, j1;
+    if (!finite(c->clip_lo) || !finite(c->clip_hi) || c->clip_lo <= 0.0f ||
+        c->clip_hi < c->clip_lo || c->mse_grid < 1 || c->mse_grid > 100000 ||
+        !mse_range(c, &j0, &j1))
+      return AR_ERR_INVALID_ARG;
+  }
   if (N < 0 || K < 0) return AR_ERR_SHAPE;
   *g = 0;
   if (N == 0 || K == 0) return AR_OK;
@@ -341,6 +373,8 @@ ar_status ar_config_default(ar_config* c) {
   c->minmax_shrink = 1.0f;
   c->clip_lo = 0.5f;
   c->clip_hi = 1.0f;
+  c->init_scale = 0;
+  c->mse_grid = 100;
   return AR_OK;
 }
 
@@ -377,6 +411,17 @@ ar_status ar_step_workspace_size(const ar_config* c, int64_t N, int64_t K, int64
   return AR_OK;
 }
 
+ar_status ar_init_clip(const ar_config* c, int32_t wdt, const void* W, int64_t N, int64_t K,
+                       float* alpha, float* beta, void* stream) {
+  int g;
+  AR_TRY(check_quant(c, N, K, &g));
+  if (!dtype_ok(wdt)) return AR_ERR_UNSUPPORTED;
+  if (g == 0) return AR_OK;
+  if (!W || !alpha || !beta || !a16(W)) return AR_ERR_INVALID_ARG;
+  return ar_launch_init_clip(wdt, W, N, K, g, grid_of(c), init_of(c), alpha, beta,
+                             static_cast<hipStream_t>(stream));
+}
+
 ar_status ar_rtn_quant(const ar_config* c, int32_t wdt, const void* W, int64_t N, int64_t K,
                        uint8_t* codes, float* scale, uint8_t* zp, void* Wq, void* stream) {
   int g;
@@ -384,7 +429,7 @@ ar_status ar_rtn_quant(const ar_config* c, int32_t wdt, const void* W, int64_t N
   if (!dtype_ok(wdt)) return AR_ERR_UNSUPPORTED;
   if (g == 0) return AR_OK;
   if (!W || !a16(W) || !a16(Wq) || !a8(codes)) return AR_ERR_INVALID_ARG;
-  return ar_launch_fakequant(wdt, W, nullptr, nullptr, nullptr, c->minmax_shrink, N, K, g,
+  return ar_launch_fakequant(wdt, W, nullptr, nullptr, nullptr, init_of(c), N, K, g,
                              grid_of(c), wdt, Wq, 0, codes, scale, zp,
                              static_cast<hipStream_t>(stream));
 }
@@ -399,7 +444,7 @@ ar_status ar_fakequant_fwd(const ar_config* c, int32_t wdt, const void* W, int64
   if (g == 0) return AR_OK;
   if (!W || !V || !alpha || !beta) return AR_ERR_INVALID_ARG;
   if (!a16(W) || !a16(V) || !a16(Wq_bf16) || !a8(codes)) return AR_ERR_INVALID_ARG;
-  return ar_launch_fakequant(wdt, W, V, alpha, beta, c->minmax_shrink, N, K, g, grid_of(c),
+  return ar_launch_fakequant(wdt, W, V, alpha, beta, init_of(c), N, K, g, grid_of(c),
                              AR_BF16, Wq_bf16, 0, codes, scale, zp,
                              static_cast<hipStream_t>(stream));
 }
@@ -434,7 +479,7 @@ ar_status ar_tune_step(const ar_config* c, const ar_state* s, const uint16_t* Xb
   AR_TRY(ar_launch_block_transpose(Xb, w.XTB, 1, Tb, K, z.nkbT, 2, st));
   AR_TRY(ar_launch_block_transpose(Yb, w.YB, 1, Tb, N, z.nkbT, (int)dsize(ydt), st));
   AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(w.WB), 0.0f, z.wb / 2, st));
-  AR_TRY(ar_launch_fakequant(s->wdt, s->W, s->V, s->alpha, s->beta, c->minmax_shrink, N, K, g,
+  AR_TRY(ar_launch_fakequant(s->wdt, s->W, s->V, s->alpha, s->beta, init_of(c), N, K, g,
                              grid_of(c), AR_BF16, w.WB, z.nkbK, nullptr, nullptr, nullptr, st));
   return enqueue_step(c, s->wdt, s->W, N, K, g, w.XB, w.XTB, w.YB, ydt, Tb, w.WB, w.dyB, w.G,
                       w.partials, w.flag, loss_out, nullptr, s->best_loss, s->V, s->alpha,
@@ -494,17 +539,15 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
   AR_TRY_C(ar_launch_block_transpose(X, w.XTB, nb, Tb, K, z.nkbT, 2, st));
   AR_TRY_C(ar_launch_block_transpose(Y, w.YB, nb, Tb, N, z.nkbT, (int)ysz, st));
   AR_TRY_C(ar_launch_fill_f32(reinterpret_cast<float*>(w.WB), 0.0f, z.wb / 2, st));
-  // initial state: V = 0, alpha = beta = minmax_shrink, best = initial, best loss = +inf
+  // initial state: V = 0, the initial clip factors, best = initial, best loss = +inf
   AR_TRY_C(ar_launch_fill_f32(w.V, 0.0f, N * K, st));
   AR_TRY_C(ar_launch_fill_f32(w.bestV, 0.0f, N * K, st));
-  AR_TRY_C(ar_launch_fill_f32(w.alpha, c->minmax_shrink, N * Gn, st));
-  AR_TRY_C(ar_launch_fill_f32(w.beta, c->minmax_shrink, N * Gn, st));
-  AR_TRY_C(ar_launch_fill_f32(w.bestA, c->minmax_shrink, N * Gn, st));
-  AR_TRY_C(ar_launch_fill_f32(w.bestB, c->minmax_shrink, N * Gn, st));
+  AR_TRY_C(ar_launch_init_clip(wdt, W, N, K, g, grid_of(c), init_of(c), w.alpha, w.beta, st));
+  AR_TRY_C(ar_launch_init_clip(wdt, W, N, K, g, grid_of(c), init_of(c), w.bestA, w.bestB, st));
   AR_TRY_C(ar_launch_fill_f32(w.best_loss, INFINITY, 1, st));
   const ArGrid gr = grid_of(c);
   if (c->iters > 0)
-    AR_TRY_C(ar_launch_fakequant(wdt, W, w.V, w.alpha, w.beta, c->minmax_shrink, N, K, g, gr,
+    AR_TRY_C(ar_launch_fakequant(wdt, W, w.V, w.alpha, w.beta, init_of(c), N, K, g, gr,
                                  AR_BF16, w.WB, z.nkbK, nullptr, nullptr, nullptr, st));
   for (int i = 0; i < c->iters; ++i) {
     const int64_t b = i % nb;
@@ -516,7 +559,7 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
         (ntimed > 0 && i % every == 0) ? &ev[(size_t)(i / every) * 6] : nullptr));
   }
   // restore the best state and quantize it (the initial state when iters = 0)
-  AR_TRY_C(ar_launch_fakequant(wdt, W, w.bestV, w.bestA, w.bestB, c->minmax_shrink, N, K, g, gr,
+  AR_TRY_C(ar_launch_fakequant(wdt, W, w.bestV, w.bestA, w.bestB, init_of(c), N, K, g, gr,
                                wdt, Wq, 0, codes, scale, zp, st));
   if (V_out && hipMemcpyAsync(V_out, w.bestV, (size_t)N * K * 4, hipMemcpyDeviceToDevice, st))
     return cleanup(AR_ERR_HIP);
@@ -691,8 +734,11 @@ ar_status ar_tune_linear_gram(const ar_config* c, int32_t wdt, const void* W, in
   AR_TRY_C(ar_launch_fill_f32(w.V[0], 0.0f, N * K, st));
   AR_TRY_C(ar_launch_fill_f32(w.V[1], 0.0f, N * K, st));
   AR_TRY_C(ar_launch_fill_f32(w.bestV, 0.0f, N * K, st));
-  for (float* p : {w.A[0], w.B[0], w.A[1], w.B[1], w.bestA, w.bestB})
-    AR_TRY_C(ar_launch_fill_f32(p, c->minmax_shrink, N * Gn, st));
+  for (int k = 0; k < 3; ++k) {
+    float* A = k < 2 ? w.A[k] : w.bestA;
+    float* B = k < 2 ? w.B[k] : w.bestB;
+    AR_TRY_C(ar_launch_init_clip(wdt, W, N, K, g, grid_of(c), init_of(c), A, B, st));
+  }
   AR_TRY_C(ar_launch_fill_f32(w.best_loss, INFINITY, 1, st));
   AR_TRY_C(ar_launch_fill_f32(reinterpret_cast<float*>(w.flag), 0.0f, 1, st));
   AR_TRY_C(ar_launch_fill_f32(reinterpret_cast<float*>(w.DB), 0.0f, q.db / 2, st));
@@ -738,7 +784,7 @@ ar_status ar_tune_linear_gram(const ar_config* c, int32_t wdt, const void* W, in
                                      w.bestB, N * K, N * Gn, st));
   }
   // restore the best state and quantize it (the initial state when iters = 0)
-  AR_TRY_C(ar_launch_fakequant(wdt, W, w.bestV, w.bestA, w.bestB, c->minmax_shrink, N, K, g, gr,
+  AR_TRY_C(ar_launch_fakequant(wdt, W, w.bestV, w.bestA, w.bestB, init_of(c), N, K, g, gr,
                                wdt, Wq, 0, codes, scale, zp, st));
   if (V_out && hipMemcpyAsync(V_out, w.bestV, (size_t)N * K * 4, hipMemcpyDeviceToDevice, st))
     return cleanup(AR_ERR_HIP);

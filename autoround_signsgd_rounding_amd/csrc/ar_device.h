@@ -75,6 +75,12 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 template <int LPG>
+__device__ __forceinline__ double group_sum_f64(double x) {
+#pragma unroll
+  for (int o = LPG / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+template <int LPG>
 __device__ __forceinline__ float group_min(float x) {
 #pragma unroll
   for (int o = LPG / 2; o > 0; o >>= 1) x = fminf(x, __shfl_xor(x, o, 64));

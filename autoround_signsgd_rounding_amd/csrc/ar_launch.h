@@ -11,6 +11,15 @@ struct ArGrid {
   int sym;
 };
 
+// Initial clip factors: alpha = beta = shrink (mse = 0), or per group the shrink
+// p_j = float32(1 - j/grid), j0 <= j <= j1, with the smallest sum of squared
+// round-to-nearest weight errors (float32 errors, float64 sum, first minimum).
+struct ArInit {
+  int mse;
+  int j0, j1, grid;
+  float shrink;
+};
+
 // Lanes per group and 8-element chunks per lane for a group of g elements.
 void ar_group_layout(int g, int* lpg, int* chunks_per_lane);
 
@@ -62,13 +71,16 @@ ar_status ar_launch_block_transpose(const void* src, void* dst, int64_t batch, i
                                     int64_t C, int64_t nkb, int elem_bytes, hipStream_t st);
 
 // Quantizer / update kernels (ar_quant.hip)
-// out_dt: dtype of Wq (AR_BF16 or AR_F32); alpha/beta NULL means the constant `shrink`,
-// V NULL means zero.
+// out_dt: dtype of Wq (AR_BF16 or AR_F32); alpha/beta NULL means the initial clip
+// factor of `init`, V NULL means zero.
 // wq_nkb > 0 writes Wq (bf16 only) in the blocked GEMM layout (rows N, reduction K).
 ar_status ar_launch_fakequant(int wdt, const void* W, const float* V, const float* alpha,
-                              const float* beta, float shrink, int64_t N, int64_t K, int g,
+                              const float* beta, const ArInit& init, int64_t N, int64_t K, int g,
                               ArGrid gr, int out_dt, void* Wq, int64_t wq_nkb, uint8_t* codes,
                               float* scale, uint8_t* zp, hipStream_t st);
+// alpha = beta = the initial clip factor of every group.
+ar_status ar_launch_init_clip(int wdt, const void* W, int64_t N, int64_t K, int g, ArGrid gr,
+                              const ArInit& init, float* alpha, float* beta, hipStream_t st);
 
 struct ArSteArgs {
   int wdt;

@@ -29,6 +29,76 @@ namespace {
 
 constexpr int NT = 256;
 
+// ------------------------------------------------------------------ initial scale
+// The MSE shrink of one group (see ArInit): for every candidate p the group is
+// quantized with V = 0 and alpha = beta = p; the float32 errors w - Ŵ are
+// squared in float32 and summed in float64 (each lane over its chunks in
+// order, then a butterfly, so every lane of the group sees the same sums).
+template <typename WT, int LPG>
+__device__ __forceinline__ float mse_search(const WT* W, int64_t base, int lig, int E, float mn,
+                                            float mx, const Grid& gr, const ArInit& in) {
+  double best = INFINITY;
+  float bp = 1.0f;
+  for (int j = in.j0; j <= in.j1; ++j) {
+    const float p = (float)(1.0 - (double)j / (double)in.grid);
+    const QP q = group_qparams(mn, mx, p, p, gr);
+    double err = 0.0;
+    for (int e = 0; e < E; ++e) {
+      float w[8];
+      load8(W + base + 8 * (lig + LPG * e), w);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float d = w[i] - quant_elem(w[i], 0.0f, q, gr).what;
+        err += (double)(d * d);
+      }
+    }
+    err = group_sum_f64<LPG>(err);
+    if (err < best) {
+      best = err;
+      bp = p;
+    }
+  }
+  return bp;
+}
+
+template <typename WT>
+struct InitArgs {
+  const WT* W;
+  int64_t ngroups, K;
+  int g, Gn, E;
+  ArGrid gr;
+  ArInit init;
+  float* alpha;
+  float* beta;
+};
+
+template <typename WT, int LPG>
+__global__ __launch_bounds__(NT) void k_init_clip(InitArgs<WT> a) {
+  const int64_t gid = ((int64_t)blockIdx.x * NT + threadIdx.x) / LPG;
+  const int lig = threadIdx.x % LPG;
+  if (gid >= a.ngroups) return;
+  const Grid gr = grid_of(a.gr);
+  const int64_t n = gid / a.Gn;
+  const int64_t base = n * a.K + (gid - n * a.Gn) * a.g;
+  float p = a.init.shrink;
+  if (a.init.mse) {
+    float mn = INFINITY, mx = -INFINITY;
+    for (int e = 0; e < a.E; ++e) {
+      float w[8];
+      load8(a.W + base + 8 * (lig + LPG * e), w);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { mn = fminf(mn, w[i]); mx = fmaxf(mx, w[i]); }
+    }
+    mn = group_min<LPG>(mn);
+    mx = group_max<LPG>(mx);
+    p = mse_search<WT, LPG>(a.W, base, lig, a.E, mn, mx, gr, a.init);
+  }
+  if (lig == 0) {
+    a.alpha[gid] = p;
+    a.beta[gid] = p;
+  }
+}
+
 // ------------------------------------------------------------------ fake-quant
 template <typename WT, typename OT>
 struct FQArgs {
@@ -36,7 +106,7 @@ struct FQArgs {
   const float* V;
   const float* alpha;
   const float* beta;
-  float shrink;
+  ArInit init;
   int64_t ngroups, K;
   int g, Gn, E;
   ArGrid gr;
@@ -65,8 +135,11 @@ __global__ __launch_bounds__(NT) void k_fakequant(FQArgs<WT, OT> a) {
   }
   mn = group_min<LPG>(mn);
   mx = group_max<LPG>(mx);
-  const float al = a.alpha ? a.alpha[gid] : a.shrink;
-  const float be = a.beta ? a.beta[gid] : a.shrink;
+  float p0 = a.init.shrink;
+  if ((!a.alpha || !a.beta) && a.init.mse)
+    p0 = mse_search<WT, LPG>(a.W, base, lig, a.E, mn, mx, gr, a.init);
+  const float al = a.alpha ? a.alpha[gid] : p0;
+  const float be = a.beta ? a.beta[gid] : p0;
   const QP p = group_qparams(mn, mx, al, be, gr);
   if (lig == 0) {
     if (a.scale) a.scale[gid] = p.s;
@@ -344,13 +417,32 @@ ar_status fq_dispatch(FQArgs<WT, OT> a, int lpg, hipStream_t st) {
 
 template <typename WT, typename OT>
 ar_status fq_make(const void* W, const float* V, const float* alpha, const float* beta,
-                  float shrink, int64_t N, int64_t K, int g, ArGrid gr, void* Wq, int64_t wq_nkb,
-                  uint8_t* codes, float* scale, uint8_t* zp, hipStream_t st) {
+                  const ArInit& init, int64_t N, int64_t K, int g, ArGrid gr, void* Wq,
+                  int64_t wq_nkb, uint8_t* codes, float* scale, uint8_t* zp, hipStream_t st) {
   int lpg, E;
   ar_group_layout(g, &lpg, &E);
-  FQArgs<WT, OT> a{static_cast<const WT*>(W), V, alpha, beta, shrink, N * (K / g), K, g,
+  FQArgs<WT, OT> a{static_cast<const WT*>(W), V, alpha, beta, init, N * (K / g), K, g,
                    (int)(K / g), E, gr, static_cast<OT*>(Wq), wq_nkb, codes, scale, zp};
   return fq_dispatch(a, lpg, st);
+}
+
+template <typename WT>
+ar_status init_make(const void* W, int64_t N, int64_t K, int g, ArGrid gr, const ArInit& init,
+                    float* alpha, float* beta, hipStream_t st) {
+  int lpg, E;
+  ar_group_layout(g, &lpg, &E);
+  InitArgs<WT> a{static_cast<const WT*>(W), N * (K / g), K, g, (int)(K / g), E, gr, init, alpha,
+                 beta};
+  const unsigned nb = blocks_for(a.ngroups * lpg);
+  switch (lpg) {
+#define AR_IC_CASE(L) \
+  case L: hipLaunchKernelGGL((k_init_clip<WT, L>), dim3(nb), dim3(NT), 0, st, a); break;
+    AR_IC_CASE(1) AR_IC_CASE(2) AR_IC_CASE(4) AR_IC_CASE(8) AR_IC_CASE(16) AR_IC_CASE(32)
+    AR_IC_CASE(64)
+#undef AR_IC_CASE
+    default: return AR_ERR_INVALID_ARG;
+  }
+  return last_status();
 }
 
 template <typename WT>
@@ -376,18 +468,24 @@ ar_status ste_make(const ArSteArgs& s, hipStream_t st) {
 }  // namespace
 
 ar_status ar_launch_fakequant(int wdt, const void* W, const float* V, const float* alpha,
-                              const float* beta, float shrink, int64_t N, int64_t K, int g,
+                              const float* beta, const ArInit& init, int64_t N, int64_t K, int g,
                               ArGrid gr, int out_dt, void* Wq, int64_t wq_nkb, uint8_t* codes,
                               float* scale, uint8_t* zp, hipStream_t st) {
   if (wq_nkb > 0 && out_dt != AR_BF16) return AR_ERR_INVALID_ARG;
   if (wdt == AR_BF16) {
     if (out_dt == AR_BF16)
-      return fq_make<uint16_t, uint16_t>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
-    return fq_make<uint16_t, float>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
+      return fq_make<uint16_t, uint16_t>(W, V, alpha, beta, init, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
+    return fq_make<uint16_t, float>(W, V, alpha, beta, init, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
   }
   if (out_dt == AR_BF16)
-    return fq_make<float, uint16_t>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
-  return fq_make<float, float>(W, V, alpha, beta, shrink, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
+    return fq_make<float, uint16_t>(W, V, alpha, beta, init, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
+  return fq_make<float, float>(W, V, alpha, beta, init, N, K, g, gr, Wq, wq_nkb, codes, scale, zp, st);
+}
+
+ar_status ar_launch_init_clip(int wdt, const void* W, int64_t N, int64_t K, int g, ArGrid gr,
+                              const ArInit& init, float* alpha, float* beta, hipStream_t st) {
+  return wdt == AR_BF16 ? init_make<uint16_t>(W, N, K, g, gr, init, alpha, beta, st)
+                        : init_make<float>(W, N, K, g, gr, init, alpha, beta, st);
 }
 
 static unsigned stage_blocks(int64_t total) {

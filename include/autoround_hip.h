@@ -67,6 +67,13 @@ typedef struct {
   float minmax_shrink;   /* initial alpha = beta ([LLMC] minmax_shrink, default 1.0)       */
   float clip_lo;         /* alpha/beta lower clamp (default 0.5)                           */
   float clip_hi;         /* alpha/beta upper clamp (default 1.0)                           */
+  int32_t init_scale;    /* initial alpha = beta ([LLMC] tuning loop: "Min-Max or MSE"):
+                            0: minmax_shrink (Min-Max); 1: MSE, per group the shrink p of
+                            the grid p_j = float32(1 - j/mse_grid) inside [clip_lo, clip_hi]
+                            whose round-to-nearest quantization has the smallest sum of
+                            squared weight errors (float32 errors, float64 sum, first
+                            minimum on ties)                                              */
+  int32_t mse_grid;      /* grid steps per unit shrink for init_scale = 1 (default 100)   */
 } ar_config;
 
 /* Per-kernel device time of one ar_tune_linear call, measured with HIP events
@@ -83,7 +90,8 @@ typedef struct {
 
 /* Fill *cfg with the [LLMC] defaults: bits 4, group_size 128, asym, nsamples 128,
    seqlen 2048, batch_samples 8, iters 200, lr 0.005, minmax_lr unset (-1),
-   minmax_shrink 1.0, clip range [0.5, 1.0]. Returns AR_ERR_INVALID_ARG on NULL. */
+   minmax_shrink 1.0, clip range [0.5, 1.0], Min-Max initial scale (mse_grid 100).
+   Returns AR_ERR_INVALID_ARG on NULL. */
 ar_status ar_config_default(ar_config* cfg);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
@@ -98,9 +106,15 @@ ar_status ar_workspace_size(const ar_config* cfg, int64_t N, int64_t K, int32_t 
 ar_status ar_step_workspace_size(const ar_config* cfg, int64_t N, int64_t K, int64_t Tb,
                                  int32_t ydt, size_t* bytes);
 
+/* Initial clip factors of every group ([LLMC] tuning loop, initial scale):
+   alpha = beta = minmax_shrink (init_scale 0) or the MSE shrink (init_scale 1).
+   alpha, beta [N, G] float32, required. N*K = 0 is a no-op. */
+ar_status ar_init_clip(const ar_config* cfg, int32_t wdt, const void* W, int64_t N, int64_t K,
+                       float* alpha, float* beta, void* stream);
+
 /* Round-to-nearest quantization ([LLMC] paper-core RTN equation): V = 0 and
-   alpha = beta = cfg->minmax_shrink; group min/max from W ([LLMC] tuning loop,
-   Min-Max initial scale).
+   the initial clip factors of ar_init_clip; group min/max from W ([LLMC] tuning
+   loop, initial scale).
    W      [N, K] of dtype wdt (AR_F32 or AR_BF16)
    codes  [N, K] uint8 in [0, 2^bits-1]        (nullable)
    scale  [N, G] float32                       (nullable)
@@ -155,7 +169,7 @@ ar_status ar_tune_step(const ar_config* cfg, const ar_state* state, const uint16
                        size_t ws_bytes, void* stream);
 
 /* The whole per-Linear tuning loop ([LLMC] tuning loop with best-loss snapshot):
-   V = 0, alpha = beta = minmax_shrink; step i uses minibatch b = i mod
+   V = 0, alpha and beta from ar_init_clip; step i uses minibatch b = i mod
    (nsamples/batch_samples), i.e. rows [b*Tb, (b+1)*Tb) of X and Y with
    Tb = batch_samples*seqlen; after cfg->iters steps the state with the lowest
    loss (strictly lower than all before it, evaluated before its update) is
@@ -172,6 +186,44 @@ ar_status ar_tune_linear(const ar_config* cfg, int32_t wdt, const void* W, int64
                          float* scale, uint8_t* zp, void* Wq, float* V_out, float* alpha_out,
                          float* beta_out, float* losses, void* ws, size_t ws_bytes,
                          ar_kernel_times* times, void* stream);
+
+/* ---- Per-layer configuration ([SGL] "2. 레이어별 개별 설정", "3. 정규식 기반
+   레이어 매칭", "4. FusedMoE와 Fused QKV 처리"). Host-only calls: strings and
+   arrays are host memory, nothing touches the GPU. -------------------------- */
+
+/* One per-layer rule. The key is an exact layer name, or a pattern when it
+   contains any of the characters * + ? ^ $ ( ) [ ] { } | \ (ECMAScript regular
+   expression, matched against the whole name). */
+typedef struct {
+  const char* key;
+  int32_t bits;         /* < 0: not set                      */
+  int32_t group_size;   /* 0: not set (-1 is "whole row")    */
+  int32_t sym;          /* < 0: not set, else 0 / 1          */
+} ar_layer_rule;
+
+typedef struct {
+  int32_t bits;         /* 16: leave the layer unquantized   */
+  int32_t group_size;
+  int32_t sym;
+} ar_layer_qconfig;
+
+/* Config of layer `name`. quantized = 0 marks a layer outside the quantized
+   set: with no rule, or an exact-name rule leaving fields unset, it gets
+   bits 16, group_size -1, sym 1. Order: exact key, then the first pattern key
+   that fully matches (keys that do not compile are skipped; unset fields from
+   *defaults), then the fallback. AR_ERR_INVALID_ARG on NULL arguments. */
+ar_status ar_resolve_layer_config(const ar_layer_rule* rules, int32_t nrules,
+                                  const ar_layer_qconfig* defaults, int32_t quantized,
+                                  const char* name, ar_layer_qconfig* out);
+
+/* Config of a fused layer: every sub-layer must resolve to the same config,
+   else AR_ERR_INVALID_ARG. With nsub > 0 the sub-layers are sub_names (a fused
+   q/k/v-style layer). With nsub = 0 they are the rule keys that start with
+   layer_name (a fused expert layer); with no such key, layer_name itself. */
+ar_status ar_resolve_fused_config(const ar_layer_rule* rules, int32_t nrules,
+                                  const ar_layer_qconfig* defaults, int32_t quantized,
+                                  const char* layer_name, const char* const* sub_names,
+                                  int32_t nsub, ar_layer_qconfig* out);
 
 /* ---- Gram form (same-input Linears) --------------------------------------
    For one Linear the quantized and the reference outputs see the same tokens,

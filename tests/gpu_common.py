@@ -44,7 +44,7 @@ def oracle_cfg(c):
     return O.Config(bits=c.bits, group_size=c.group_size, sym=bool(c.sym), nsamples=c.nsamples,
                     seqlen=c.seqlen, batch_samples=c.batch_samples, iters=c.iters, lr=c.lr,
                     minmax_lr=c.minmax_lr, minmax_shrink=c.minmax_shrink, clip_lo=c.clip_lo,
-                    clip_hi=c.clip_hi)
+                    clip_hi=c.clip_hi, init=c.init, mse_grid=c.mse_grid)
 
 
 def rel_norm(a, b):

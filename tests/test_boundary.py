@@ -44,6 +44,7 @@ def test_config_default_and_strings():
         (4, 128, 0, 128, 2048, 8, 200)
     assert abs(c.lr - 0.005) < 1e-9 and c.minmax_lr < 0 and c.minmax_shrink == 1.0
     assert (c.clip_lo, c.clip_hi) == (0.5, 1.0)
+    assert (c.init_scale, c.mse_grid) == (0, 100)
     assert ar.lib.ar_config_default(None) == INV
     for s in (0, 1, 2, 3, 4, 6, 99):
         assert len(ar.lib.ar_status_string(s)) > 0
@@ -72,6 +73,23 @@ def test_rtn_validation():
     assert rtn(c, Wq=P_MIS) == INV
     assert rtn(c, N=0) == OK          # empty: no-op, nothing launched
     assert rtn(c, K=0) == OK
+
+
+def test_init_scale_validation():
+    assert rtn(cfg(init="mse")[0], N=0) == OK
+    c, cc = cfg(init="mse")
+    cc.init_scale = 2
+    assert rtn(ctypes.byref(cc)) == INV
+    assert rtn(cfg(init="mse", mse_grid=0)[0]) == INV
+    assert rtn(cfg(init="mse", clip_lo=0.91, clip_hi=0.99, minmax_shrink=0.95, mse_grid=10)[0]) == INV
+    assert rtn(cfg(init="mse", clip_lo=0.0)[0]) == INV
+    # min-max init ignores the grid (validation only: the workspace query launches nothing)
+    assert _ws(cfg(mse_grid=0)[0])[0] == OK
+    assert _ws(cfg(init="mse", mse_grid=0)[0])[0] == INV
+    f = ar.lib.ar_init_clip
+    assert f(cfg(init="mse")[0], 1, P, 8, 128, NULL, P, NULL) == INV
+    assert f(cfg(init="mse")[0], 1, P_MIS, 8, 128, P, P, NULL) == INV
+    assert f(cfg(init="mse")[0], 1, P, 0, 128, P, P, NULL) == OK
 
 
 def test_fakequant_validation():
