@@ -529,6 +529,31 @@ def unpack(qweight, qzeros, bits: int, N: int, K: int):
     return codes, zp
 
 
+# ------------------------------------------------------------------ W{2,3,4,8}A16 product
+def dequantize(qweight, qzeros, scale, bits: int, group_size: int, N: int, K: int):
+    """Ŵ [N, K] float32 from the packed format ([SGL] "설계 근거": AutoRound
+    checkpoints reuse GPTQ/AWQ packing; the dequantisation Ŵ = s·(q - zp) of
+    [LLMC] _fake_quantize_with_offset): codes and zero-points unpacked (zp =
+    2^(bits-1) when qzeros is None, the symmetric grid), scale [N, G] float32,
+    then s·(q - zp) in float32."""
+    g = K if group_size == -1 else group_size
+    if qzeros is None:
+        codes, _ = unpack(qweight, np.zeros((1, N * bits // 32), np.uint32), bits, N, K)
+        zp = np.full((N, K // g), 2 ** (bits - 1), np.int64)
+    else:
+        codes, zp = unpack(qweight, qzeros, bits, N, K)
+    s_e = np.repeat(np.asarray(scale, F32), g, axis=1)
+    zp_e = np.repeat(np.asarray(zp, F32), g, axis=1)
+    return (s_e * (codes.astype(F32) - zp_e)).astype(F32)
+
+
+def dequant_matmul(X, qweight, qzeros, scale, bits: int, group_size: int, N: int, K: int):
+    """Y = X·bf16(Ŵ)ᵀ [M, N] in float64 (bf16 Ŵ: the operand the tuning loop's
+    forward product uses; X is taken as given, bf16 values)."""
+    what = dequantize(qweight, qzeros, scale, bits, group_size, N, K)
+    return np.asarray(X, F64) @ bf16(what).astype(F64).T
+
+
 # ------------------------------------------------------------------ brute force
 def brute_force_rounding(W, X, Y, qp: QParams, bits: int, group_size: int):
     """Exhaustive optimum over every floor/ceil choice of W/s (the rounding

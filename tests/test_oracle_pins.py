@@ -574,3 +574,39 @@ def test_fused_configs():
     assert O.resolve_fused_config(rules, DEF, True, "f.experts") == DEF
     with pytest.raises(ValueError):
         O.resolve_fused_config(rules + [("e.experts.2.w1", {"bits": 2})], DEF, True, "e.experts")
+
+
+# ------------------------------------------------------------------ dequantisation
+@pytest.mark.parametrize("bits,sym", [(2, False), (3, False), (4, True), (8, False)])
+def test_dequantize_inverts_the_quantizer(bits, sym):
+    """Packing the codes and zero-points of a state and dequantizing gives back
+    the quantizer's own Ŵ bit for bit."""
+    rng = np.random.default_rng(60 + bits)
+    N, K, g = 32, 256, 64
+    W = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    cfg = O.Config(bits=bits, group_size=g, sym=sym)
+    codes, s, zp, what = O.rtn_quant(W, cfg)
+    qw, qz = O.pack(codes, zp, bits)
+    got = O.dequantize(qw, None if sym else qz, s, bits, g, N, K)
+    np.testing.assert_array_equal(got, what)
+
+
+def test_dequant_matmul_hand_example():
+    """4-bit, one group of 8 per row, written out by hand (rows 2..7 have zero
+    scale; zero-points pack 8 rows to a word)."""
+    codes = np.zeros((8, 8), np.uint8)
+    codes[0] = [0, 1, 2, 3, 4, 5, 6, 7]
+    codes[1] = [15, 14, 13, 12, 11, 10, 9, 8]
+    zp = np.zeros((8, 1), np.uint8)
+    zp[0, 0], zp[1, 0] = 3, 8
+    scale = np.zeros((8, 1), F32)
+    scale[0, 0], scale[1, 0] = 0.5, 0.25
+    qw, qz = O.pack(codes, zp, 4)
+    # word of row 0: codes 0..7 LSB first -> 0x76543210; row 1 -> 0x89ABCDEF
+    assert qw[0, 0] == 0x76543210 and qw[0, 1] == 0x89ABCDEF
+    assert qz[0, 0] == 0x83                                  # zp 3 then 8, LSB first
+    X = np.array([[1, 0, 0, 0, 0, 0, 0, 2]], F32)
+    # row 0: 0.5*(0-3) + 2*0.5*(7-3) = -1.5 + 4 = 2.5; row 1: 0.25*(15-8) + 2*0.25*(8-8) = 1.75
+    Y = O.dequant_matmul(X, qw, qz, scale, 4, 8, 8, 8)
+    np.testing.assert_allclose(Y[0, :2], [2.5, 1.75])
+    assert not Y[0, 2:].any()
