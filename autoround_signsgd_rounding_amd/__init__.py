@@ -28,6 +28,7 @@ EXPORTS = (
     "ar_rtn_quant", "ar_fakequant_fwd", "ar_tune_step", "ar_tune_linear", "ar_pack", "ar_unpack",
     "ar_gram_workspace_size", "ar_gram_step_workspace_size", "ar_tune_step_gram",
     "ar_tune_linear_gram", "ar_init_clip", "ar_resolve_layer_config", "ar_resolve_fused_config",
+    "ar_dequant_gemm_workspace_size", "ar_dequant_gemm",
 )
 
 
@@ -104,6 +105,8 @@ def _load():
                                     ctypes.POINTER(ArLayerQConfig), i32, ctypes.c_char_p,
                                     ctypes.POINTER(ctypes.c_char_p), i32,
                                     ctypes.POINTER(ArLayerQConfig)],
+        "ar_dequant_gemm_workspace_size": [i32, i64, i64, i64, ctypes.POINTER(sz)],
+        "ar_dequant_gemm": [i32, i32, vp, i64, i64, vp, vp, vp, i64, vp, i32, vp, sz, vp],
         "ar_pack": [i32, vp, vp, i64, i64, i64, vp, vp, vp],
         "ar_unpack": [i32, vp, vp, i64, i64, i64, vp, vp, vp],
     }
@@ -359,6 +362,28 @@ def tune_linear(W, X, Y, cfg: Config, *, want_state=True, want_wq=False, timed=F
               _ptr(workspace), workspace.numel(), ctypes.byref(times) if timed else None,
               _stream(stream)), name)
     return TuneOutput(codes, scale, zp, Wq, V, a, b, losses[:cfg.iters], times)
+
+
+def dequant_gemm(X, qweight, qzeros, scale, bits: int, group_size: int, N: int, *,
+                 out_dtype=None, workspace=None, stream=None):
+    """Y [M, N] = X·bf16(Ŵ)ᵀ from the packed format (ar_dequant_gemm). X [M, K]
+    bf16; qzeros None for the symmetric grid; scale [N, G] float32."""
+    torch = _torch()
+    _dev(X, qweight, qzeros, scale)
+    M, K = X.shape
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bf16")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    Y = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    need = ctypes.c_size_t()
+    _check(lib.ar_dequant_gemm_workspace_size(bits, M, N, K, ctypes.byref(need)),
+           "ar_dequant_gemm_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=X.device)
+    _check(lib.ar_dequant_gemm(bits, group_size, _ptr(X), M, K, _ptr(qweight), _ptr(qzeros),
+                               _ptr(scale), N, _ptr(Y), _dt(Y), _ptr(workspace),
+                               workspace.numel(), _stream(stream)), "ar_dequant_gemm")
+    return Y
 
 
 def pack(codes, zp, bits: int, stream=None):

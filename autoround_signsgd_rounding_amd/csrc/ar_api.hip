@@ -816,6 +816,66 @@ ar_status ar_tune_linear_gram(const ar_config* c, int32_t wdt, const void* W, in
   return cleanup(AR_OK);
 }
 
+// ---- W-bit x bf16 product
+static constexpr int64_t kGemvMaxM = 16;
+
+static size_t dequant_ws(int64_t M, int64_t N, int64_t K) {
+  if (M <= kGemvMaxM) return pad256((size_t)ar_dq_slices(N, K) * M * N * 4);
+  Carver c{nullptr};
+  c.take<uint16_t>((size_t)arblk::row_tiles(M) * arblk::k_blocks(K) * arblk::BLOCK_ELEMS * 2);
+  c.take<uint16_t>((size_t)arblk::row_tiles(N) * arblk::k_blocks(K) * arblk::BLOCK_ELEMS * 2);
+  return c.off;
+}
+
+static ar_status check_dequant(int32_t bits, int64_t M, int64_t N, int64_t K) {
+  if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8)) return AR_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxLd * 64 || N >= (int64_t(1) << 31) / 256)
+    return AR_ERR_SHAPE;
+  if (K != 0 && (K % 8 != 0 || (K * bits) % 32 != 0 || K >= kMaxLd)) return AR_ERR_SHAPE;
+  return AR_OK;
+}
+
+ar_status ar_dequant_gemm_workspace_size(int32_t bits, int64_t M, int64_t N, int64_t K,
+                                         size_t* bytes) {
+  if (!bytes) return AR_ERR_INVALID_ARG;
+  AR_TRY(check_dequant(bits, M, N, K));
+  *bytes = (M == 0 || N == 0 || K == 0) ? 0 : dequant_ws(M, N, K);
+  return AR_OK;
+}
+
+ar_status ar_dequant_gemm(int32_t bits, int32_t group_size, const uint16_t* X, int64_t M,
+                          int64_t K, const int32_t* qweight, const int32_t* qzeros,
+                          const float* scale, int64_t N, void* Y, int32_t ydt, void* ws,
+                          size_t ws_bytes, void* stream) {
+  AR_TRY(check_dequant(bits, M, N, K));
+  if (!dtype_ok(ydt)) return AR_ERR_UNSUPPORTED;
+  if (group_size != -1 && group_size <= 0) return AR_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return AR_OK;
+  if (K == 0) return AR_ERR_SHAPE;
+  const int64_t g = group_size == -1 ? K : group_size;
+  if (g % 8 != 0) return AR_ERR_UNSUPPORTED;
+  if (K % g != 0) return AR_ERR_SHAPE;
+  if (qzeros && (N * bits) % 32 != 0) return AR_ERR_SHAPE;
+  if (!X || !qweight || !scale || !Y || !ws) return AR_ERR_INVALID_ARG;
+  if (!a16(X) || !a16(ws) || !a8(qweight)) return AR_ERR_INVALID_ARG;
+  if (ws_bytes < dequant_ws(M, N, K)) return AR_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M <= kGemvMaxM)
+    return ar_launch_dq_gemv(bits, qweight, qzeros, scale, N, K, (int)g, X, (int)M,
+                             static_cast<float*>(ws), Y, ydt, st);
+  Carver c{static_cast<uint8_t*>(ws)};
+  uint16_t* XB = c.take<uint16_t>((size_t)arblk::row_tiles(M) * arblk::k_blocks(K) *
+                                  arblk::BLOCK_ELEMS * 2);
+  uint16_t* WB = c.take<uint16_t>((size_t)arblk::row_tiles(N) * arblk::k_blocks(K) *
+                                  arblk::BLOCK_ELEMS * 2);
+  const int64_t nkb = arblk::k_blocks(K);
+  AR_TRY(ar_launch_block_copy(X, XB, 1, M, K, nkb, st));
+  AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(WB),
+                            0.0f, arblk::row_tiles(N) * nkb * arblk::BLOCK_ELEMS / 2, st));
+  AR_TRY(ar_launch_dequant_blocked(bits, qweight, qzeros, scale, N, K, (int)g, WB, st));
+  return ar_launch_gemm_out(XB, WB, Y, ydt, M, N, K, st);
+}
+
 ar_status ar_pack(int32_t bits, const uint8_t* codes, const uint8_t* zp, int64_t N, int64_t K,
                   int64_t G, int32_t* qweight, int32_t* qzeros, void* stream) {
   if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8)) return AR_ERR_UNSUPPORTED;

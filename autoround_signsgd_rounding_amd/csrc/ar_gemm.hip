@@ -380,6 +380,53 @@ ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void*
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 
+// Plain product epilogue (the dequantized-weight GEMM): Y[i, j] = acc for
+// i < M (rows of P), j < N (rows of Q), row-major, float32 or bf16.
+struct EpiOut {
+  static constexpr int kPrefetch = 0;
+  void* Y;
+  int64_t M, N;
+  int ydt;
+
+  __device__ __forceinline__ const void* prefetch_base(int, int) const { return Y; }
+  __device__ __forceinline__ void pre(uint8_t*) const {}
+  __device__ __forceinline__ void operator()(f32x16_t (&acc)[4][4], int ti, int tj, int wi, int wj,
+                                             int lane, uint8_t*, int) const {
+    const int64_t m0 = (int64_t)ti * BM, n0 = (int64_t)tj * BN;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+      const int64_t n = n0 + wj * 128 + bj * 32 + (lane & 31);
+      if (n < N) {
+#pragma unroll
+        for (int bi = 0; bi < 4; ++bi) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t m = m0 + wi * 128 + bi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m < M) {
+              if (ydt == AR_BF16)
+                static_cast<uint16_t*>(Y)[m * N + n] = (uint16_t)bf16_bits(acc[bi][bj][r]);
+              else
+                static_cast<float*>(Y)[m * N + n] = acc[bi][bj][r];
+            }
+          }
+        }
+      }
+    }
+  }
+};
+
+ar_status ar_launch_gemm_out(const uint16_t* XB, const uint16_t* WB, void* Y, int ydt, int64_t M,
+                             int64_t N, int64_t K, hipStream_t st) {
+  GemmArgs a;
+  a.P = XB; a.Q = WB;
+  a.nkb = (int)arblk::k_blocks(K);
+  a.tilesI = (int)arblk::row_tiles(M);
+  a.tilesJ = (int)arblk::row_tiles(N);
+  EpiOut e{Y, M, N, ydt};
+  hipLaunchKernelGGL(k_gemm<EpiOut>, dim3(a.tilesI * a.tilesJ), dim3(NTHR), 0, st, a, e);
+  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
+}
+
 // The Gram-form product D·H gets its own type so that profiles name it apart
 // from the weight-gradient product (same code).
 struct EpiGramP : EpiWgrad {};

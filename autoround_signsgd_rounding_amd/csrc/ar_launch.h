@@ -63,6 +63,9 @@ ar_status ar_launch_gemm_gram(const uint16_t* DB, const uint16_t* HB, float* P, 
 ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* G, int64_t N,
                                int64_t K, int64_t Tb, float scale, const ArLossIn& loss,
                                hipStream_t st);
+// Y[M, N] = XB·WBᵀ (XB rows M, WB rows N, reduction K), row-major f32 or bf16.
+ar_status ar_launch_gemm_out(const uint16_t* XB, const uint16_t* WB, void* Y, int ydt, int64_t M,
+                             int64_t N, int64_t K, hipStream_t st);
 // blocked staging: batch of row-major [R, KR] -> blocked (rows R, reduction KR)
 ar_status ar_launch_block_copy(const uint16_t* src, uint16_t* dst, int64_t batch, int64_t R,
                                int64_t KR, int64_t nkb, hipStream_t st);
@@ -107,6 +110,18 @@ struct ArSteArgs {
 ar_status ar_launch_ste_update(const ArSteArgs& a, hipStream_t st);
 
 ar_status ar_launch_fill_f32(float* p, float v, int64_t n, hipStream_t st);
+
+// W-bit x bf16 product on the packed format (ar_dequant.hip). g % 8 == 0.
+// Dequantized bf16 Ŵ into the blocked operand (rows N, reduction K).
+ar_status ar_launch_dequant_blocked(int bits, const int32_t* qweight, const int32_t* qzeros,
+                                    const float* scale, int64_t N, int64_t K, int g, uint16_t* WB,
+                                    hipStream_t st);
+// Split-K slices of the small-M product; its workspace is slices*M*N floats.
+int ar_dq_slices(int64_t N, int64_t K);
+// Y[M, N] = X·bf16(Ŵ)ᵀ for M <= 16.
+ar_status ar_launch_dq_gemv(int bits, const int32_t* qweight, const int32_t* qzeros,
+                            const float* scale, int64_t N, int64_t K, int g, const uint16_t* X,
+                            int M, float* part, void* Y, int ydt, hipStream_t st);
 
 // Gram-form step (ar_gram.hip). D operands are blocked with rows N and reduction
 // 3K ([D_hi | D_hi | D_lo]); H operands with rows K and reduction 3K

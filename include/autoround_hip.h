@@ -187,6 +187,26 @@ ar_status ar_tune_linear(const ar_config* cfg, int32_t wdt, const void* W, int64
                          float* beta_out, float* losses, void* ws, size_t ws_bytes,
                          ar_kernel_times* times, void* stream);
 
+/* ---- W{2,3,4,8} x bf16 product on the packed format ------------------------
+   Y = X·bf16(Ŵ)ᵀ with Ŵ = s·(q - zp) read from ar_pack's format ([SGL] "설계
+   근거": AutoRound checkpoints reuse GPTQ/AWQ packing; [LLMC]
+   _fake_quantize_with_offset for the dequantisation): the deployment side of the
+   tuned codes. The bf16 Ŵ is the operand the tuning loop's forward product uses.
+   X [M, K] bf16 row-major; qweight [K*bits/32, N] int32 and qzeros
+   [G, N*bits/32] int32 as ar_pack writes them (qzeros NULL: symmetric grid,
+   zp = 2^(bits-1)); scale [N, G] float32 (ar_tune_linear's layout); Y [M, N]
+   row-major, ydt AR_F32 or AR_BF16. float32 accumulation. group_size as in
+   ar_config (-1: whole row); K*bits % 32 == 0, K % group = 0, group % 8 == 0;
+   with qzeros N*bits % 32 == 0. M <= 16 reads the packed words directly
+   (split-K, slices summed in a fixed order); larger M dequantizes once into a
+   blocked bf16 operand and runs the MFMA product. M = 0 or N = 0 is a no-op. */
+ar_status ar_dequant_gemm_workspace_size(int32_t bits, int64_t M, int64_t N, int64_t K,
+                                         size_t* bytes);
+ar_status ar_dequant_gemm(int32_t bits, int32_t group_size, const uint16_t* X, int64_t M,
+                          int64_t K, const int32_t* qweight, const int32_t* qzeros,
+                          const float* scale, int64_t N, void* Y, int32_t ydt, void* ws,
+                          size_t ws_bytes, void* stream);
+
 /* ---- Per-layer configuration ([SGL] "2. 레이어별 개별 설정", "3. 정규식 기반
    레이어 매칭", "4. FusedMoE와 Fused QKV 처리"). Host-only calls: strings and
    arrays are host memory, nothing touches the GPU. -------------------------- */

@@ -1,0 +1,105 @@
+"""GPU parity of the W{2,3,4,8} x bf16 product on the packed format
+(ar_dequant_gemm) against the oracle's dequant_matmul (float64 on the same
+bf16 Ŵ), on both paths (M <= 16 split-K reading the packed words; larger M
+through the blocked MFMA product), and end to end: a tuned layer's packed
+output reproduces the product with its own Ŵ."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from gpu_common import F32, bf16_dev, dev, log, rel_norm, to_np, weight_dev
+
+pytestmark = pytest.mark.gpu
+ar = pytest.importorskip("autoround_signsgd_rounding_amd")
+
+
+def _packed(N, K, bits, g, sym, seed):
+    """Random codes / zero-points / scales of a plausible layer, packed."""
+    rng = np.random.default_rng(seed)
+    G = 1 if g == -1 else K // g
+    codes = rng.integers(0, 2 ** bits, (N, K), dtype=np.uint8)
+    zp = rng.integers(0, 2 ** bits, (N, G), dtype=np.uint8)
+    scale = (rng.uniform(0.5, 2.0, (N, G)) * 0.01).astype(F32)
+    qw, qz = O.pack(codes, zp, bits)
+    if sym:
+        qz = None
+    return qw, qz, scale
+
+
+def _gpu_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(dev())
+
+
+CASES = [
+    # M, N, K, bits, g, sym, out
+    (1, 4096, 4096, 4, 128, False, "f32"),
+    (5, 256, 512, 2, 32, False, "f32"),
+    (16, 96, 384, 3, 128, False, "bf16"),
+    (3, 64, 256, 8, -1, True, "f32"),
+    (17, 256, 512, 4, 64, True, "f32"),       # smallest M on the MFMA path
+    (300, 520, 200, 8, 40, False, "f32"),     # ragged tiles and reduction
+    (257, 128, 768, 3, 96, False, "bf16"),
+    (64, 160, 256, 2, -1, False, "f32"),
+]
+
+
+@pytest.mark.parametrize("M,N,K,bits,g,sym,out", CASES)
+def test_dequant_gemm_parity(M, N, K, bits, g, sym, out):
+    log(f"dequant_gemm M={M} N={N} K={K} b{bits} g{g} sym={sym} out={out}")
+    qw, qz, scale = _packed(N, K, bits, g, sym, seed=M + N + K + bits)
+    rng = np.random.default_rng(M * 3 + K)
+    Xb = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(F32))
+    Xf = synth.bf16_bits_to_f32(Xb)
+    Y = ar.dequant_gemm(bf16_dev(Xb), _gpu_i32(qw), None if qz is None else _gpu_i32(qz),
+                        torch.from_numpy(scale).to(dev()), bits, g, N,
+                        out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = O.dequant_matmul(Xf, qw, qz, scale, bits, g, N, K)
+    got = to_np(Y).astype(np.float64)
+    err = rel_norm(got, ref)
+    log(f"  rel err {err:.2e}")
+    if out == "f32":
+        assert err <= 1e-5
+        assert np.abs(got - ref).max() <= 1e-5 * np.abs(ref).max()
+    else:
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max())
+
+
+def test_tuned_layer_round_trip():
+    """Tune (toy 256->256, W4 g64), pack, and multiply through the packed format:
+    the product equals X·bf16(Ŵ)ᵀ with the tuning loop's own Ŵ."""
+    w = synth.WORKLOADS["toy_256"]
+    case = synth.make_workload_case(w)
+    Y = synth.reference_outputs(case)
+    cfg = ar.Config(bits=w.bits, group_size=w.group_size, nsamples=w.nsamples, seqlen=w.seqlen,
+                    batch_samples=w.batch_samples, iters=w.iters)
+    Xd = bf16_dev(case.X_bits)
+    out = ar.tune_linear(weight_dev(case), Xd, torch.from_numpy(Y).to(dev()), cfg, want_wq=True)
+    qw, qz = ar.pack(out.codes, out.zp, w.bits)
+    for M in (4, 256):
+        Yq = ar.dequant_gemm(Xd[:M], qw, qz, out.scale, w.bits, w.group_size, w.N)
+        torch.cuda.synchronize()
+        Wq = O.bf16(to_np(out.Wq)).astype(np.float64)
+        ref = synth.bf16_bits_to_f32(case.X_bits[:M]).astype(np.float64) @ Wq.T
+        log(f"  M={M}: rel err {rel_norm(to_np(Yq), ref):.2e}")
+        assert rel_norm(to_np(Yq), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("M", [1, 16, 2048])
+def test_dequant_gemm_q_proj_shape(M):
+    """Llama-7B q_proj 4096->4096, W4 g128 asym: the decode sizes in full, the
+    prefill size on 64 sampled rows of X."""
+    N = K = 4096
+    qw, qz, scale = _packed(N, K, 4, 128, False, seed=M)
+    rng = np.random.default_rng(M)
+    Xb = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(F32))
+    Y = ar.dequant_gemm(bf16_dev(Xb), _gpu_i32(qw), _gpu_i32(qz),
+                        torch.from_numpy(scale).to(dev()), 4, 128, N)
+    torch.cuda.synchronize()
+    rows = np.arange(M) if M <= 16 else np.sort(rng.choice(M, 64, replace=False))
+    ref = O.dequant_matmul(synth.bf16_bits_to_f32(Xb[rows]), qw, qz, scale, 4, 128, N, K)
+    err = rel_norm(to_np(Y)[rows], ref)
+    log(f"  M={M}: rel err {err:.2e}")
+    assert err <= 1e-5
