@@ -364,22 +364,31 @@ def tune_linear(W, X, Y, cfg: Config, *, want_state=True, want_wq=False, timed=F
     return TuneOutput(codes, scale, zp, Wq, V, a, b, losses[:cfg.iters], times)
 
 
-def dequant_gemm(X, qweight, qzeros, scale, bits: int, group_size: int, N: int, *,
-                 out_dtype=None, workspace=None, stream=None):
-    """Y [M, N] = X·bf16(Ŵ)ᵀ from the packed format (ar_dequant_gemm). X [M, K]
-    bf16; qzeros None for the symmetric grid; scale [N, G] float32."""
-    torch = _torch()
-    _dev(X, qweight, qzeros, scale)
-    M, K = X.shape
-    if X.dtype != torch.bfloat16:
-        raise ValueError("X must be bf16")
-    out_dtype = torch.float32 if out_dtype is None else out_dtype
-    Y = torch.empty((M, N), dtype=out_dtype, device=X.device)
+def dequant_gemm_workspace_size(bits: int, M: int, N: int, K: int) -> int:
     need = ctypes.c_size_t()
     _check(lib.ar_dequant_gemm_workspace_size(bits, M, N, K, ctypes.byref(need)),
            "ar_dequant_gemm_workspace_size")
+    return need.value
+
+
+def dequant_gemm(X, qweight, qzeros, scale, bits: int, group_size: int, N: int, *,
+                 out_dtype=None, out=None, workspace=None, stream=None):
+    """Y [M, N] = X·bf16(Ŵ)ᵀ from the packed format (ar_dequant_gemm). X [M, K]
+    bf16; qzeros None for the symmetric grid; scale [N, G] float32. ``out`` and
+    ``workspace`` may be given to avoid allocations."""
+    torch = _torch()
+    _dev(X, qweight, qzeros, scale, out)
+    M, K = X.shape
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bf16")
+    if out is None:
+        out_dtype = torch.float32 if out_dtype is None else out_dtype
+        Y = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    else:
+        Y = out
     if workspace is None:
-        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=X.device)
+        need = dequant_gemm_workspace_size(bits, M, N, K)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
     _check(lib.ar_dequant_gemm(bits, group_size, _ptr(X), M, K, _ptr(qweight), _ptr(qzeros),
                                _ptr(scale), N, _ptr(Y), _dt(Y), _ptr(workspace),
                                workspace.numel(), _stream(stream)), "ar_dequant_gemm")

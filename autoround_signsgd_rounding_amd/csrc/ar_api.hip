@@ -820,7 +820,7 @@ ar_status ar_tune_linear_gram(const ar_config* c, int32_t wdt, const void* W, in
 static constexpr int64_t kGemvMaxM = 16;
 
 static size_t dequant_ws(int64_t M, int64_t N, int64_t K) {
-  if (M <= kGemvMaxM) return pad256((size_t)ar_dq_slices(N, K) * M * N * 4);
+  if (M <= kGemvMaxM) return pad256((size_t)ar_dq_slices(N, K, M) * M * N * 4);
   Carver c{nullptr};
   c.take<uint16_t>((size_t)arblk::row_tiles(M) * arblk::k_blocks(K) * arblk::BLOCK_ELEMS * 2);
   c.take<uint16_t>((size_t)arblk::row_tiles(N) * arblk::k_blocks(K) * arblk::BLOCK_ELEMS * 2);
@@ -856,6 +856,8 @@ ar_status ar_dequant_gemm(int32_t bits, int32_t group_size, const uint16_t* X, i
   if (g % 8 != 0) return AR_ERR_UNSUPPORTED;
   if (K % g != 0) return AR_ERR_SHAPE;
   if (qzeros && (N * bits) % 32 != 0) return AR_ERR_SHAPE;
+  if (K * bits / 32 * N >= (int64_t(1) << 31) || (K / g) * N >= (int64_t(1) << 31))
+    return AR_ERR_SHAPE;   // packed arrays are indexed with 32-bit offsets
   if (!X || !qweight || !scale || !Y || !ws) return AR_ERR_INVALID_ARG;
   if (!a16(X) || !a16(ws) || !a8(qweight)) return AR_ERR_INVALID_ARG;
   if (ws_bytes < dequant_ws(M, N, K)) return AR_ERR_WORKSPACE;

@@ -13,7 +13,8 @@ steps; `cpu_baseline` is the CPU oracle timed on a bounded sample.
 
     python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--workload llama7b_q_proj]
 
-detail.gram reports the same job in the Gram form (ar_tune_linear_gram).
+detail.gram reports the same job in the Gram form (ar_tune_linear_gram);
+detail.dequant_gemm the tuned codes through the packed-format product.
 """
 import argparse
 import json
@@ -90,6 +91,70 @@ def _cpu_baseline(case, Yd, w, steps=2):
                       f"{el / steps:.2f} s/step; a 200-iteration run extrapolates to "
                       f"{200 * el / steps / 60:.1f} min",
             "host_cpus": os.cpu_count(), "host": platform.processor() or platform.machine()}
+
+
+def _dequant_run(ar, torch, X, out, w, reps=20):
+    """The tuned layer's packed codes through ar_dequant_gemm: decode sizes
+    (M = 1, 16; bound by reading the packed weight, reported as GB/s of
+    algorithmic bytes against 8 TB/s) and one minibatch of prefill (M = Tb;
+    TFLOP/s against the bf16 peak). Buffers are allocated once; the decode
+    calls are captured `reps` at a time in a HIP graph and the replays timed
+    with HIP events, so host call overhead is not in the figure."""
+    qw, qz = ar.pack(out.codes, out.zp, w.bits)
+    G = w.K // w.group_size
+    res = {}
+    stream = torch.cuda.current_stream()
+    for M in (1, 16, w.Tb):
+        Xm = X[:M]
+        Yo = torch.empty((M, w.N), dtype=torch.float32, device=X.device)
+        ws = torch.empty(max(ar.dequant_gemm_workspace_size(w.bits, M, w.N, w.K), 256),
+                         dtype=torch.uint8, device=X.device)
+
+        def call():
+            ar.dequant_gemm(Xm, qw, qz, out.scale, w.bits, w.group_size, w.N, out=Yo,
+                            workspace=ws)
+        call()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        if M <= 16:
+            g = torch.cuda.CUDAGraph()
+            s2 = torch.cuda.Stream()
+            with torch.cuda.stream(s2):
+                with torch.cuda.graph(g, stream=s2):
+                    for _ in range(reps):
+                        call()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            n_rep = 5
+            e0.record(stream)
+            for _ in range(n_rep):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / (n_rep * reps)
+        else:
+            n = 5
+            e0.record(stream)
+            for _ in range(n):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / n
+        if M <= 16:
+            nbytes = (w.N * w.K * w.bits // 8 + w.N * G * 4 + G * w.N * w.bits // 8
+                      + M * w.K * 2 + M * w.N * 4)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            res[f"M{M}"] = {"us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
+        else:
+            tf = 2.0 * M * w.N * w.K / (ms * 1e-3) / 1e12
+            res[f"M{M}"] = {"us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+                            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del Yo, ws
+    res["config"] = f"W{w.bits} g{w.group_size} {w.N}x{w.K}, tuned codes, float32 output"
+    return res
 
 
 def _gram_run(ar, torch, W, X, Y, cfg, w, args):
@@ -274,6 +339,7 @@ def main():
             "input_gen_s": round(t_gen, 1),
         },
     }
+    line["detail"]["dequant_gemm"] = _dequant_run(ar, torch, X, recs[-1][3], w)
     if not args.no_gram:
         line["detail"]["gram"] = _gram_run(ar, torch, W, X, Y, cfg, w, args)
     if not args.no_cpu_baseline:

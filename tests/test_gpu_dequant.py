@@ -103,3 +103,32 @@ def test_dequant_gemm_q_proj_shape(M):
     err = rel_norm(to_np(Y)[rows], ref)
     log(f"  M={M}: rel err {err:.2e}")
     assert err <= 1e-5
+
+
+def test_decode_product_under_graph_capture():
+    """The small-M path captured in a HIP graph: every replay (with eager work
+    and synchronizations between replays) equals the eager result bit for bit."""
+    N, K, M = 512, 1024, 8
+    qw, qz, scale = _packed(N, K, 4, 128, False, seed=99)
+    rng = np.random.default_rng(5)
+    Xd = bf16_dev(synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(F32)))
+    args = (_gpu_i32(qw), _gpu_i32(qz), torch.from_numpy(scale).to(dev()), 4, 128, N)
+    eager = ar.dequant_gemm(Xd, *args)
+    Y = torch.empty_like(eager)
+    ws = torch.empty(max(ar.dequant_gemm_workspace_size(4, M, N, K), 256), dtype=torch.uint8,
+                     device=dev())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            ar.dequant_gemm(Xd, *args, out=Y, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        Y.fill_(float(i + 7))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, eager), i
+        junk = ar.dequant_gemm(Xd[:1], *args)          # eager work between replays
+        torch.cuda.synchronize()
+        del junk
