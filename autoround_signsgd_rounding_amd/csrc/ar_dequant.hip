@@ -96,7 +96,9 @@ __global__ __launch_bounds__(NT) void k_dequant_blocked(DqArgs a, uint16_t* WB, 
 constexpr int GEMV_COLS = 64;      // columns per workgroup (one per lane)
 constexpr int GEMV_MMAX = 16;
 constexpr int GEMV_BATCH = 16;     // chunks whose packed words are in flight together
-constexpr int GEMV_XLDS = 65536;   // bytes of LDS for the X slice
+// Bytes of LDS for the X slice of a workgroup with at most MT rows: small
+// buckets keep it small so that many workgroups share a CU.
+__host__ __device__ constexpr int gemv_xlds(int MT) { return MT >= 4 ? 65536 : 16384 * MT; }
 
 // One workgroup: 64 columns x one K slice. The slice of X (M rows) is staged in
 // LDS once; each wave takes every 4th chunk of 8 codes and issues the packed
@@ -109,14 +111,14 @@ template <int BITS, int MT>
 __global__ __launch_bounds__(NT) void k_dq_gemv(DqArgs a, const uint16_t* X, int M, float* part,
                                                 int chunks_per_slice) {
   __shared__ float red[4][MT][GEMV_COLS];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[GEMV_XLDS / 2];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[gemv_xlds(MT) / 2];
   constexpr uint32_t MASK = (1u << BITS) - 1u;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int N = (int)a.N, K = (int)a.K;
   const int n = blockIdx.x * GEMV_COLS + lane;
   const int c_begin = blockIdx.y * chunks_per_slice;
   const int c_end = min(c_begin + chunks_per_slice, K / 8);
-  const int nc = c_end - c_begin;   // chunks in this slice (nc * M * 16 <= GEMV_XLDS)
+  const int nc = c_end - c_begin;   // chunks in this slice (nc * M * 16 <= gemv_xlds(MT))
   for (int i = threadIdx.x; i < nc * M; i += NT) {
     const int m = i / nc, c = i - m * nc;
     *reinterpret_cast<u32x4_t*>(xs + (m * nc + c) * 8) =
@@ -246,9 +248,12 @@ DqArgs dq_args(const int32_t* qweight, const int32_t* qzeros, const float* scale
 
 }  // namespace
 
+// Row bucket of the small-M product.
+static int gemv_bucket(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+
 // Slices of the small-M product: about two workgroups per CU, at least 16
 // chunks of 8 codes per slice, and few enough chunks that the X slice fits
-// the LDS stage.
+// the bucket's LDS stage.
 int ar_dq_slices(int64_t N, int64_t K, int64_t M) {
   const int64_t colblocks = (N + GEMV_COLS - 1) / GEMV_COLS;
   const int64_t chunks = K / 8;
@@ -256,7 +261,7 @@ int ar_dq_slices(int64_t N, int64_t K, int64_t M) {
   const int64_t maxS = chunks / 16;
   if (S > maxS) S = maxS;
   if (S < 1) S = 1;
-  const int64_t max_cps = GEMV_XLDS / (16 * (M > 0 ? M : 1));
+  const int64_t max_cps = gemv_xlds(gemv_bucket(M)) / (16 * (M > 0 ? M : 1));
   while ((chunks + S - 1) / S > max_cps) ++S;
   return (int)S;
 }

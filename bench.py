@@ -154,7 +154,54 @@ def _dequant_run(ar, torch, X, out, w, reps=20):
                             "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
         del Yo, ws
     res["config"] = f"W{w.bits} g{w.group_size} {w.N}x{w.K}, tuned codes, float32 output"
+    res["M1_large"] = _decode_large(ar, torch, reps)
     return res
+
+
+def _decode_large(ar, torch, reps, N=29568, K=8192, bits=4, g=128):
+    """One-token product on a Qwen2.5-72B up_proj-sized W4 layer (random codes:
+    the speed does not depend on their values), graph-timed like the decode
+    sizes above; 121 MB of packed weight make the HBM roofline the honest bound."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    G = K // g
+    qw = torch.randint(-2 ** 31, 2 ** 31 - 1, (K * bits // 32, N), dtype=torch.int32, device=dev,
+                       generator=gen)
+    qz = torch.randint(-2 ** 31, 2 ** 31 - 1, (G, N * bits // 32), dtype=torch.int32, device=dev,
+                       generator=gen)
+    sc = torch.rand((N, G), device=dev, generator=gen) * 0.01
+    X = torch.randn((1, K), device=dev, generator=gen).to(torch.bfloat16)
+    Y = torch.empty((1, N), device=dev)
+    ws = torch.empty(max(ar.dequant_gemm_workspace_size(bits, 1, N, K), 256), dtype=torch.uint8,
+                     device=dev)
+
+    def call():
+        ar.dequant_gemm(X, qw, qz, sc, bits, g, N, out=Y, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        with torch.cuda.graph(graph, stream=s2):
+            for _ in range(reps):
+                call()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    for _ in range(5):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (5 * reps)
+    nbytes = N * K * bits // 8 + N * G * 4 + G * N * bits // 8 + K * 2 + N * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"shape": f"W{bits} g{g} {N}x{K}", "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
 
 
 def _gram_run(ar, torch, W, X, Y, cfg, w, args):
