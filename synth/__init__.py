@@ -208,3 +208,81 @@ def reference_outputs_torch(case: Case, device, rows: slice | None = None):
         y = (xc @ W64.T).to(torch.float32)
         out[c0 - r0:c1 - r0] = y.to(torch.bfloat16) if bf else y
     return out
+
+
+# ---------------------------------------------------------------- decoder block
+@dataclasses.dataclass(frozen=True)
+class BlockDims:
+    """A Llama-style decoder block: hidden D, heads H (head_dim D/H), MLP width
+    F; calibration of nsamples sequences of seqlen tokens."""
+    name: str
+    D: int
+    H: int
+    F: int
+    seqlen: int
+    nsamples: int
+    rms_eps: float = 1e-6
+    rope_theta: float = 10000.0
+    sigma_w: float = 0.02
+    seed: int = 0
+
+    @property
+    def M(self) -> int:
+        return self.nsamples * self.seqlen
+
+    @property
+    def Dh(self) -> int:
+        return self.D // self.H
+
+
+BLOCKS = {
+    b.name: b
+    for b in (
+        BlockDims("toy_block", D=256, H=4, F=512, seqlen=64, nsamples=4),
+        BlockDims("llama7b_block", D=4096, H=32, F=11008, seqlen=2048, nsamples=16),
+    )
+}
+
+# Linear layers of the block in tuning order: (name, out features, in features)
+BLOCK_LINEARS = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+
+
+def block_linear_shape(b: BlockDims, name: str):
+    return {"q_proj": (b.D, b.D), "k_proj": (b.D, b.D), "v_proj": (b.D, b.D),
+            "o_proj": (b.D, b.D), "gate_proj": (b.F, b.D), "up_proj": (b.F, b.D),
+            "down_proj": (b.D, b.F)}[name]
+
+
+@dataclasses.dataclass
+class BlockCase:
+    dims: BlockDims
+    W_bits: dict          # name -> bf16 bits [out, in]
+    norm_bits: tuple      # (attention norm, MLP norm) bf16 bits [D]
+    H_bits: np.ndarray    # block input hidden states, bf16 bits [M, D]
+
+
+def make_block_case(b: BlockDims, nsamples: int | None = None) -> BlockCase:
+    """Draw one block's weights and its calibration input (one stream, in this
+    order): the seven Linear weights N(0, sigma_w) in BLOCK_LINEARS order, each
+    with rint(0.005·in) outlier input columns ×10; the two RMSNorm weights
+    1 + N(0, 0.05); the hidden states N(0, 1) [M, D] with rint(0.01·D) outlier
+    channels ×20, drawn in row chunks. Everything is cast to bf16 (RNE)."""
+    rng = np.random.default_rng(b.seed)
+    W = {}
+    for name in BLOCK_LINEARS:
+        N, K = block_linear_shape(b, name)
+        cols = rng.choice(K, size=int(np.rint(0.005 * K)), replace=False)
+        w = rng.normal(0.0, b.sigma_w, size=(N, K)).astype(np.float32)
+        w[:, cols] *= np.float32(10.0)
+        W[name] = f32_to_bf16_bits(w)
+    norms = tuple(f32_to_bf16_bits((1.0 + 0.05 * rng.standard_normal(b.D)).astype(np.float32))
+                  for _ in range(2))
+    M = (nsamples if nsamples is not None else b.nsamples) * b.seqlen
+    chs = rng.choice(b.D, size=int(np.rint(0.01 * b.D)), replace=False)
+    Hb = np.empty((M, b.D), dtype=np.uint16)
+    for r0 in range(0, M, CHUNK_ROWS):
+        r1 = min(M, r0 + CHUNK_ROWS)
+        hc = rng.standard_normal(size=(r1 - r0, b.D), dtype=np.float32)
+        hc[:, chs] *= np.float32(20.0)
+        Hb[r0:r1] = f32_to_bf16_bits(hc)
+    return BlockCase(dims=b, W_bits=W, norm_bits=norms, H_bits=Hb)
