@@ -28,7 +28,8 @@ EXPORTS = (
     "ar_rtn_quant", "ar_fakequant_fwd", "ar_tune_step", "ar_tune_linear", "ar_pack", "ar_unpack",
     "ar_gram_workspace_size", "ar_gram_step_workspace_size", "ar_tune_step_gram",
     "ar_tune_linear_gram", "ar_init_clip", "ar_resolve_layer_config", "ar_resolve_fused_config",
-    "ar_dequant_gemm_workspace_size", "ar_dequant_gemm",
+    "ar_dequant_gemm_workspace_size", "ar_dequant_gemm", "ar_block_workspace_size",
+    "ar_block_forward", "ar_tune_block",
 )
 
 
@@ -73,6 +74,27 @@ class ArLayerQConfig(ctypes.Structure):
                 ("sym", ctypes.c_int32)]
 
 
+class ArBlockDims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int64), ("heads", ctypes.c_int64), ("inter", ctypes.c_int64),
+                ("seqlen", ctypes.c_int64), ("nsamples", ctypes.c_int64),
+                ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+
+
+class ArBlockWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("Wq", "Wk", "Wv", "Wo", "Wg", "Wu", "Wd",
+                                               "norm_attn", "norm_mlp")]
+
+
+class ArBlockOutputs(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p * 7), ("scale", ctypes.c_void_p * 7),
+                ("zp", ctypes.c_void_p * 7), ("Wq", ctypes.c_void_p * 7),
+                ("losses", ctypes.c_void_p * 7), ("out_fp", ctypes.c_void_p),
+                ("out_q", ctypes.c_void_p)]
+
+
+BLOCK_LINEARS = ("q_proj", "k_proj", "v_proj", "o_proj", "gate_proj", "up_proj", "down_proj")
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
@@ -107,6 +129,11 @@ def _load():
                                     ctypes.POINTER(ArLayerQConfig)],
         "ar_dequant_gemm_workspace_size": [i32, i64, i64, i64, ctypes.POINTER(sz)],
         "ar_dequant_gemm": [i32, i32, vp, i64, i64, vp, vp, vp, i64, vp, i32, vp, sz, vp],
+        "ar_block_workspace_size": [cfgp, ctypes.POINTER(ArBlockDims), ctypes.POINTER(sz)],
+        "ar_block_forward": [ctypes.POINTER(ArBlockDims), ctypes.POINTER(ArBlockWeights), vp, vp,
+                             vp, sz, vp],
+        "ar_tune_block": [cfgp, ctypes.POINTER(ArBlockDims), ctypes.POINTER(ArBlockWeights), vp,
+                          vp, i32, ctypes.POINTER(ArBlockOutputs), vp, sz, vp],
         "ar_pack": [i32, vp, vp, i64, i64, i64, vp, vp, vp],
         "ar_unpack": [i32, vp, vp, i64, i64, i64, vp, vp, vp],
     }
@@ -456,4 +483,67 @@ def resolve_fused_config(rules, defaults, quantized: bool, layer_name: str, sub_
                                        layer_name.encode(), names, len(subs),
                                        ctypes.byref(out)), "ar_resolve_fused_config")
     return out.bits, out.group_size, bool(out.sym)
+
+
+# ------------------------------------------------------------------ decoder block
+def block_dims(D, H, F, seqlen, nsamples, rms_eps=1e-6, rope_theta=10000.0) -> ArBlockDims:
+    return ArBlockDims(D, H, F, seqlen, nsamples, rms_eps, rope_theta)
+
+
+def _block_weights(W: dict, norms):
+    _dev(*W.values(), *norms)
+    return ArBlockWeights(*[W[n].data_ptr() for n in BLOCK_LINEARS],
+                          norms[0].data_ptr(), norms[1].data_ptr())
+
+
+def block_forward(h, W: dict, norms, dims: ArBlockDims, stream=None):
+    """The decoder block's forward (ar_block_forward): h [M, D] bf16, W maps
+    the Linear names to bf16 [out, in] tensors, norms = (attention, MLP) bf16 [D]."""
+    torch = _torch()
+    _dev(h)
+    bw = _block_weights(W, norms)
+    need = ctypes.c_size_t()
+    _check(lib.ar_block_workspace_size(None, ctypes.byref(dims), ctypes.byref(need)),
+           "ar_block_workspace_size")
+    ws = torch.empty(need.value, dtype=torch.uint8, device=h.device)
+    out = torch.empty_like(h)
+    _check(lib.ar_block_forward(ctypes.byref(dims), ctypes.byref(bw), _ptr(h), _ptr(out),
+                                _ptr(ws), ws.numel(), _stream(stream)), "ar_block_forward")
+    return out
+
+
+def tune_block(h, W: dict, norms, dims: ArBlockDims, cfg: Config, *, quanted_input=True,
+               h_q=None, stream=None):
+    """Sequential tuning of the block's Linears (ar_tune_block). Returns a dict
+    name -> (codes, scale, zp, Wq, losses) and the block outputs (fp, quantized)."""
+    torch = _torch()
+    _dev(h, h_q)
+    dev = h.device
+    bw = _block_weights(W, norms)
+    cc = cfg.c()
+    need = ctypes.c_size_t()
+    _check(lib.ar_block_workspace_size(ctypes.byref(cc), ctypes.byref(dims),
+                                       ctypes.byref(need)), "ar_block_workspace_size")
+    ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    res = {}
+    outs = ArBlockOutputs()
+    for i, n in enumerate(BLOCK_LINEARS):
+        N, K = W[n].shape
+        G = cfg.G(K)
+        t = (torch.empty((N, K), dtype=torch.uint8, device=dev),
+             torch.empty((N, G), dtype=torch.float32, device=dev),
+             torch.empty((N, G), dtype=torch.uint8, device=dev),
+             torch.empty((N, K), dtype=torch.bfloat16, device=dev),
+             torch.empty(max(cfg.iters, 1), dtype=torch.float32, device=dev))
+        res[n] = t
+        outs.codes[i], outs.scale[i], outs.zp[i], outs.Wq[i], outs.losses[i] = \
+            [x.data_ptr() for x in t]
+    out_fp = torch.empty_like(h)
+    out_q = torch.empty_like(h)
+    outs.out_fp, outs.out_q = out_fp.data_ptr(), out_q.data_ptr()
+    _check(lib.ar_tune_block(ctypes.byref(cc), ctypes.byref(dims), ctypes.byref(bw), _ptr(h),
+                             _ptr(h_q), int(quanted_input), ctypes.byref(outs), _ptr(ws),
+                             ws.numel(), _stream(stream)), "ar_tune_block")
+    res = {n: (c, s, z, w, l[:cfg.iters]) for n, (c, s, z, w, l) in res.items()}
+    return res, out_fp, out_q
 

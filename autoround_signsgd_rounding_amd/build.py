@@ -17,7 +17,7 @@ OUT = os.path.join(PKG, "libautoround_hip.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["ar_api.hip", "ar_gemm.hip", "ar_gram.hip", "ar_quant.hip", "ar_dequant.hip",
-           "ar_layers.cpp"]
+           "ar_block.hip", "ar_layers.cpp"]
 
 # -ffp-contract=off: the quantizer's float32 steps must round exactly as
 # written (no fused multiply-adds). Packed-fp32 instructions are disabled.

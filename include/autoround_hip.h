@@ -207,6 +207,66 @@ ar_status ar_dequant_gemm(int32_t bits, int32_t group_size, const uint16_t* X, i
                           const float* scale, int64_t N, void* Y, int32_t ydt, void* ws,
                           size_t ws_bytes, void* stream);
 
+/* ---- Sequential block-wise tuning with quantized inputs --------------------
+   [LLMC] tuning loop (each Linear of a subgraph tuned in turn on its captured
+   inputs and targets), parameter table and "enable_quanted_input 모드" (the
+   previous layers' quantized output as input), design point 3 (layer by
+   layer). The pages do not show the block; a Llama-style decoder block is
+   used: a = RMSNorm(h); q, k, v = a·W{q,k,v}ᵀ; rotate-half rotary embedding
+   on q and k (theta rope_theta, position = token index within its sequence);
+   causal softmax(q·kᵀ/sqrt(Dh))·v per sequence and head; h1 = h + attn·Woᵀ;
+   m = RMSNorm(h1); z = SiLU(m·Wgᵀ)·(m·Wuᵀ); out = h1 + z·Wdᵀ. bf16
+   activations between operations. */
+typedef struct {
+  int64_t hidden;       /* D                                  */
+  int64_t heads;        /* H; head_dim D/H must be 64 or 128  */
+  int64_t inter;        /* F (MLP width)                      */
+  int64_t seqlen;       /* tokens per calibration sequence    */
+  int64_t nsamples;     /* calibration sequences              */
+  float rms_eps;
+  float rope_theta;
+} ar_block_dims;
+
+typedef struct {        /* bf16 [out, in] row-major; norms bf16 [D] */
+  const uint16_t *Wq, *Wk, *Wv, *Wo, *Wg, *Wu, *Wd;
+  const uint16_t *norm_attn, *norm_mlp;
+} ar_block_weights;
+
+/* Per Linear, in the order q, k, v, o, gate, up, down: codes [N, K] uint8,
+   scale [N, G] float32, zp [N, G] uint8, Wq [N, K] bf16 (all required),
+   losses [iters] float32 (nullable). out_fp / out_q [M, D] bf16: the block
+   output with the original / the tuned weights (nullable). */
+typedef struct {
+  uint8_t* codes[7];
+  float* scale[7];
+  uint8_t* zp[7];
+  uint16_t* Wq[7];
+  float* losses[7];
+  uint16_t* out_fp;
+  uint16_t* out_q;
+} ar_block_outputs;
+
+/* Workspace bytes for ar_block_forward (cfg NULL) or ar_tune_block (cfg set;
+   cfg->nsamples * cfg->seqlen must equal the block's token count). */
+ar_status ar_block_workspace_size(const ar_config* cfg, const ar_block_dims* dims, size_t* bytes);
+
+/* The block's forward on h [nsamples*seqlen, D] bf16 -> out (same shape). */
+ar_status ar_block_forward(const ar_block_dims* dims, const ar_block_weights* w,
+                           const uint16_t* h, uint16_t* out, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Tune the block's seven Linears in order q, k, v, o, gate, up, down, each with
+   ar_tune_linear on target Y = its full-precision output (the block with the
+   original weights on h) and input X = its input in the quantized pipeline
+   (quanted_input != 0: the block on h_q with the Linears tuned so far replaced
+   by their bf16 Ŵ; h_q NULL means h) or in the full-precision pipeline
+   (quanted_input = 0). cfg as for ar_tune_linear with nsamples*seqlen = the
+   block's tokens. Blocks until the host has enqueued all work. */
+ar_status ar_tune_block(const ar_config* cfg, const ar_block_dims* dims,
+                        const ar_block_weights* w, const uint16_t* h, const uint16_t* h_q,
+                        int32_t quanted_input, const ar_block_outputs* outs, void* ws,
+                        size_t ws_bytes, void* stream);
+
 /* ---- Per-layer configuration ([SGL] "2. 레이어별 개별 설정", "3. 정규식 기반
    레이어 매칭", "4. FusedMoE와 Fused QKV 처리"). Host-only calls: strings and
    arrays are host memory, nothing touches the GPU. -------------------------- */
