@@ -14,7 +14,8 @@ steps; `cpu_baseline` is the CPU oracle timed on a bounded sample.
     python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--workload llama7b_q_proj]
 
 detail.gram reports the same job in the Gram form (ar_tune_linear_gram);
-detail.dequant_gemm the tuned codes through the packed-format product.
+detail.dequant_gemm the tuned codes through the packed-format product;
+detail.block sequential block-wise tuning of a Llama-7B-shaped decoder block.
 """
 import argparse
 import json
@@ -204,6 +205,43 @@ def _decode_large(ar, torch, reps, N=29568, K=8192, bits=4, g=128):
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
 
 
+def _block_run(ar, torch, iters=200):
+    """Sequential block-wise tuning with quantized inputs (ar_tune_block) of a
+    Llama-7B-shaped decoder block (D 4096, 32 heads, F 11008) on 16 synthetic
+    sequences of 2048 tokens, W4 g128, 200 iterations per Linear on minibatches
+    of 8 sequences: wall time for the whole block (both pipelines' forwards and
+    the seven tuning loops) after one untimed single-iteration call."""
+    dims = synth.BLOCKS["llama7b_block"]
+    c = synth.make_block_case(dims)
+    dev = torch.device("cuda:0")
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    W = {n: bf(c.W_bits[n]) for n in ar.BLOCK_LINEARS}
+    norms = tuple(bf(x) for x in c.norm_bits)
+    h = bf(c.H_bits)
+    bd = ar.block_dims(dims.D, dims.H, dims.F, dims.seqlen, dims.nsamples, dims.rms_eps,
+                       dims.rope_theta)
+    res = {}
+    for it in (1, iters):
+        cfg = ar.Config(bits=4, group_size=128, nsamples=dims.nsamples, seqlen=dims.seqlen,
+                        batch_samples=8, iters=it)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out, out_fp, out_q = ar.tune_block(h, W, norms, bd, cfg, quanted_input=True)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        res[it] = (el, out, out_fp, out_q)
+    el, out, out_fp, out_q = res[iters]
+    mse = float(((out_q.float() - out_fp.float()) ** 2).mean())
+    return {"workload": f"{dims.name}: D {dims.D}, H {dims.H}, F {dims.F}, {dims.nsamples}x"
+                        f"{dims.seqlen} tokens, W4 g128, {iters} iters per Linear, quantized inputs",
+            "seconds": round(el, 3), "seconds_1_iter": round(res[1][0], 3),
+            "tune_iters_per_s": round(7 * iters / el, 1),
+            "best_loss": {n: float(out[n][4].min()) for n in ar.BLOCK_LINEARS},
+            "block_out_mse": mse}
+
+
 def _gram_run(ar, torch, W, X, Y, cfg, w, args):
     """The same job in the Gram form (ar_tune_linear_gram + ar_pack): per-minibatch
     statistics staged inside the call, then one D·H product (2·N·K·3K FLOP on a
@@ -260,6 +298,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gram", action="store_true",
                     help="skip the Gram-form run reported under detail.gram")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the block-wise tuning run reported under detail.block")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -387,6 +427,8 @@ def main():
         },
     }
     line["detail"]["dequant_gemm"] = _dequant_run(ar, torch, X, recs[-1][3], w)
+    if not args.no_block:
+        line["detail"]["block"] = _block_run(ar, torch)
     if not args.no_gram:
         line["detail"]["gram"] = _gram_run(ar, torch, W, X, Y, cfg, w, args)
     if not args.no_cpu_baseline:
