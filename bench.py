@@ -300,6 +300,9 @@ def main():
                     help="skip the Gram-form run reported under detail.gram")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the block-wise tuning run reported under detail.block")
+    ap.add_argument("--block-only", action="store_true",
+                    help="only run the block-wise tuning measurement and print its record "
+                         "(for a kernel-trace profile of that workload alone)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -322,6 +325,9 @@ def main():
     import torch
     import autoround_signsgd_rounding_amd as ar
 
+    if args.block_only:
+        print(json.dumps({"block": _block_run(ar, torch)}), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     t_gen = time.time()

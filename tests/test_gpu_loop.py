@@ -119,16 +119,19 @@ def test_loop_is_deterministic():
         np.testing.assert_array_equal(x, y)
 
 
-def test_q_proj_200_iters_against_oracle_golden():
-    """Llama-7B q_proj 4096->4096, W4 g128, 200 iterations over 16 minibatches
-    of 8x2048 tokens, against the oracle's own 200-iteration run stored by
-    tests/golden/make_golden.py (codes of 128 sampled rows, loss trajectory)."""
-    path = os.path.join(GOLDEN, "tune_llama7b_q_proj.npz")
+@pytest.mark.parametrize("name", ["llama7b_q_proj", "llama7b_down_proj", "llama7b_gate_proj"])
+def test_200_iters_against_oracle_golden(name):
+    """A Llama-7B linear (q_proj 4096->4096 W4 g128 asym; down_proj
+    11008->4096 W2 g128 asym; gate_proj 4096->11008 W3 g128 sym), 200
+    iterations over 16 minibatches of 8x2048 tokens, against the oracle's own
+    200-iteration run stored by tests/golden/make_golden.py (codes of 128
+    sampled rows, loss trajectory)."""
+    path = os.path.join(GOLDEN, f"tune_{name}.npz")
     if not os.path.exists(path):
         pytest.skip("golden file not generated")
     gold = np.load(path)
-    w = synth.WORKLOADS["llama7b_q_proj"]
-    log("tune_linear llama7b_q_proj 200 iters: generating inputs")
+    w = synth.WORKLOADS[name]
+    log(f"tune_linear {name} 200 iters: generating inputs")
     case = synth.make_workload_case(w)
     Xd = bf16_dev(case.X_bits)
     Yd = synth.reference_outputs_torch(case, dev())
