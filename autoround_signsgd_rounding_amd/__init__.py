@@ -127,7 +127,7 @@ def _load():
                                     ctypes.POINTER(ArLayerQConfig), i32, ctypes.c_char_p,
                                     ctypes.POINTER(ctypes.c_char_p), i32,
                                     ctypes.POINTER(ArLayerQConfig)],
-        "ar_dequant_gemm_workspace_size": [i32, i64, i64, i64, ctypes.POINTER(sz)],
+        "ar_dequant_gemm_workspace_size": [i32, i32, i64, i64, i64, ctypes.POINTER(sz)],
         "ar_dequant_gemm": [i32, i32, vp, i64, i64, vp, vp, vp, i64, vp, i32, vp, sz, vp],
         "ar_block_workspace_size": [cfgp, ctypes.POINTER(ArBlockDims), ctypes.POINTER(sz)],
         "ar_block_forward": [ctypes.POINTER(ArBlockDims), ctypes.POINTER(ArBlockWeights), vp, vp,
@@ -391,9 +391,9 @@ def tune_linear(W, X, Y, cfg: Config, *, want_state=True, want_wq=False, timed=F
     return TuneOutput(codes, scale, zp, Wq, V, a, b, losses[:cfg.iters], times)
 
 
-def dequant_gemm_workspace_size(bits: int, M: int, N: int, K: int) -> int:
+def dequant_gemm_workspace_size(bits: int, group_size: int, M: int, N: int, K: int) -> int:
     need = ctypes.c_size_t()
-    _check(lib.ar_dequant_gemm_workspace_size(bits, M, N, K, ctypes.byref(need)),
+    _check(lib.ar_dequant_gemm_workspace_size(bits, group_size, M, N, K, ctypes.byref(need)),
            "ar_dequant_gemm_workspace_size")
     return need.value
 
@@ -414,7 +414,7 @@ def dequant_gemm(X, qweight, qzeros, scale, bits: int, group_size: int, N: int, 
     else:
         Y = out
     if workspace is None:
-        need = dequant_gemm_workspace_size(bits, M, N, K)
+        need = dequant_gemm_workspace_size(bits, group_size, M, N, K)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
     _check(lib.ar_dequant_gemm(bits, group_size, _ptr(X), M, K, _ptr(qweight), _ptr(qzeros),
                                _ptr(scale), N, _ptr(Y), _dt(Y), _ptr(workspace),

@@ -819,8 +819,8 @@ ar_status ar_tune_linear_gram(const ar_config* c, int32_t wdt, const void* W, in
 // ---- W-bit x bf16 product
 static constexpr int64_t kGemvMaxM = 16;
 
-static size_t dequant_ws(int64_t M, int64_t N, int64_t K) {
-  if (M <= kGemvMaxM) return pad256((size_t)ar_dq_slices(N, K, M) * M * N * 4);
+static size_t dequant_ws(int bits, int64_t M, int64_t N, int64_t K, int64_t g) {
+  if (M <= kGemvMaxM) return pad256((size_t)ar_dq_slices(bits, N, K, M, g) * M * N * 4);
   Carver c{nullptr};
   c.take<uint16_t>((size_t)arblk::row_tiles(M) * arblk::k_blocks(K) * arblk::BLOCK_ELEMS * 2);
   c.take<uint16_t>((size_t)arblk::row_tiles(N) * arblk::k_blocks(K) * arblk::BLOCK_ELEMS * 2);
@@ -835,11 +835,25 @@ static ar_status check_dequant(int32_t bits, int64_t M, int64_t N, int64_t K) {
   return AR_OK;
 }
 
-ar_status ar_dequant_gemm_workspace_size(int32_t bits, int64_t M, int64_t N, int64_t K,
-                                         size_t* bytes) {
+static ar_status dequant_group(int32_t group_size, int64_t K, int64_t* g) {
+  if (group_size != -1 && group_size <= 0) return AR_ERR_INVALID_ARG;
+  *g = group_size == -1 ? K : group_size;
+  if (*g % 8 != 0) return AR_ERR_UNSUPPORTED;
+  if (K % *g != 0) return AR_ERR_SHAPE;
+  return AR_OK;
+}
+
+ar_status ar_dequant_gemm_workspace_size(int32_t bits, int32_t group_size, int64_t M, int64_t N,
+                                         int64_t K, size_t* bytes) {
   if (!bytes) return AR_ERR_INVALID_ARG;
   AR_TRY(check_dequant(bits, M, N, K));
-  *bytes = (M == 0 || N == 0 || K == 0) ? 0 : dequant_ws(M, N, K);
+  if (M == 0 || N == 0 || K == 0) {
+    *bytes = 0;
+    return AR_OK;
+  }
+  int64_t g = 0;
+  AR_TRY(dequant_group(group_size, K, &g));
+  *bytes = dequant_ws(bits, M, N, K, g);
   return AR_OK;
 }
 
@@ -852,15 +866,14 @@ ar_status ar_dequant_gemm(int32_t bits, int32_t group_size, const uint16_t* X, i
   if (group_size != -1 && group_size <= 0) return AR_ERR_INVALID_ARG;
   if (M == 0 || N == 0) return AR_OK;
   if (K == 0) return AR_ERR_SHAPE;
-  const int64_t g = group_size == -1 ? K : group_size;
-  if (g % 8 != 0) return AR_ERR_UNSUPPORTED;
-  if (K % g != 0) return AR_ERR_SHAPE;
+  int64_t g = 0;
+  AR_TRY(dequant_group(group_size, K, &g));
   if (qzeros && (N * bits) % 32 != 0) return AR_ERR_SHAPE;
   if (K * bits / 32 * N >= (int64_t(1) << 31) || (K / g) * N >= (int64_t(1) << 31))
     return AR_ERR_SHAPE;   // packed arrays are indexed with 32-bit offsets
   if (!X || !qweight || !scale || !Y || !ws) return AR_ERR_INVALID_ARG;
   if (!a16(X) || !a16(ws) || !a8(qweight)) return AR_ERR_INVALID_ARG;
-  if (ws_bytes < dequant_ws(M, N, K)) return AR_ERR_WORKSPACE;
+  if (ws_bytes < dequant_ws(bits, M, N, K, g)) return AR_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (M <= kGemvMaxM)
     return ar_launch_dq_gemv(bits, qweight, qzeros, scale, N, K, (int)g, X, (int)M,

@@ -9,10 +9,13 @@
 // n's codes along K, LSB first (3-bit codes straddle words); qzeros [G, N·b/32]
 // the same along N (NULL: the symmetric grid, zp = 2^(b−1)); scale [N, G] f32.
 //
-// Small M (decode) is bound by reading the packed weight: a split-K GEMV reads
-// each column's words once, coalesced along N, and keeps M ≤ 16 accumulators
-// per lane; slices are summed in a fixed order. Larger M dequantizes once into
-// the blocked bf16 operand and runs the MFMA GEMM.
+// Small M (decode) streams the packed words once: each code is dequantized
+// once and the M <= 16 rows of X share it through the MFMA unit; K slices are
+// summed in a fixed order. Larger M dequantizes once into the blocked bf16
+// operand and runs the MFMA GEMM.
+#include <mutex>
+#include <vector>
+
 #include "ar_blocked.h"
 #include "ar_device.h"
 #include "ar_launch.h"
@@ -93,112 +96,247 @@ __global__ __launch_bounds__(NT) void k_dequant_blocked(DqArgs a, uint16_t* WB, 
 }
 
 // ------------------------------------------------------------------ small-M product
-constexpr int GEMV_COLS = 64;      // columns per workgroup (one per lane)
-constexpr int GEMV_MMAX = 16;
-constexpr int GEMV_BATCH = 16;     // chunks whose packed words are in flight together
-// Bytes of LDS for the X slice of a workgroup with at most MT rows: small
-// buckets keep it small so that many workgroups share a CU.
-__host__ __device__ constexpr int gemv_xlds(int MT) { return MT >= 4 ? 65536 : 16384 * MT; }
+// The packed words are streamed once and every code is dequantized once; the
+// M <= 16 rows of X share it through v_mfma_f32_16x16x32_bf16 (rows beyond M
+// repeat row M - 1 and are discarded), so the arithmetic per code is only the
+// dequantization.
+//
+// Workgroup: 256 columns (64 per wave) x one K slice. Lane l of a wave owns
+// the four adjacent columns c = 4·(l % 16) .. +3 of its wave's 64, read as one
+// 16-byte load per packed word, and in each 32-wide step the chunk of 8 codes
+// at k = 32·step + 8·(l / 16). Those 8 codes of column c + i are the lane's B
+// operand of MFMA i, whose output column l % 16 is therefore column c + i; the
+// A operand is the same 8 k of X row l % 16, read from an LDS copy of the
+// slice. (A and B take one k assignment per lane, so the sum is over the
+// chunk's k whatever order the unit adds them in.)
+//
+// bf16 Ŵ = s·(q − zp) costs three VALU operations per code at 4 bits: bytes
+// q + 128 − zp are formed four at a time (mask, add of a per-group constant;
+// no carries, as q + 128 − zp lies in [113, 143]), converted by
+// v_cvt_f32_ubyte, and fma(q + 128 − zp, s, −128·s) gives s·(q − zp) rounded
+// once, as the product of an exact integer and s is; v_cvt_pk_bf16_f32 rounds
+// two to bf16 (nearest even). 2 and 3 bits extract each code with a bit-field
+// extract instead; 8-bit codes are bytes, converted and then s·(q − zp).
+constexpr int DQ_COLS = 256;        // columns per workgroup
+constexpr int DQ_GSTRIDE = DQ_COLS + 4;   // floats per staged group row (bank spread)
+constexpr int DQ_WG_COST = 96;      // fixed cost of a workgroup (staging), in units of k
+constexpr int DQ_X_LDS = 32768;     // bytes for the X slice
+constexpr int DQ_G_LDS = 32768;     // bytes for the group constants (s, −128·s, zero-point term)
+constexpr int DQ_MAX_LK = 4096;     // longest slice (group-row table of Lk / 8 entries)
 
-// One workgroup: 64 columns x one K slice. The slice of X (M rows) is staged in
-// LDS once; each wave takes every 4th chunk of 8 codes and issues the packed
-// words, zero-points and scales of GEMV_BATCH chunks before using any, so one
-// memory round trip covers a batch. MT >= M is the compile-time row count.
-// Index arithmetic is 32-bit (the host keeps the packed arrays below 2^31
-// elements). The four waves' sums are added in wave order; slices are added by
-// k_dq_reduce in slice order.
-template <int BITS, int MT>
-__global__ __launch_bounds__(NT) void k_dq_gemv(DqArgs a, const uint16_t* X, int M, float* part,
-                                                int chunks_per_slice) {
-  __shared__ float red[4][MT][GEMV_COLS];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[gemv_xlds(MT) / 2];
-  constexpr uint32_t MASK = (1u << BITS) - 1u;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int N = (int)a.N, K = (int)a.K;
-  const int n = blockIdx.x * GEMV_COLS + lane;
-  const int c_begin = blockIdx.y * chunks_per_slice;
-  const int c_end = min(c_begin + chunks_per_slice, K / 8);
-  const int nc = c_end - c_begin;   // chunks in this slice (nc * M * 16 <= gemv_xlds(MT))
-  for (int i = threadIdx.x; i < nc * M; i += NT) {
-    const int m = i / nc, c = i - m * nc;
-    *reinterpret_cast<u32x4_t*>(xs + (m * nc + c) * 8) =
-        *reinterpret_cast<const u32x4_t*>(X + (int64_t)m * K + (c_begin + c) * 8);
+// Per-(group, column) zero-point term of the dequantization below.
+template <int BITS>
+__device__ __forceinline__ uint32_t zp_term(uint32_t zp) {
+  if constexpr (BITS == 4) return (128u - zp) * 0x01010101u;
+  else if constexpr (BITS == 8) return __float_as_uint((float)zp);
+  else return 128u - zp;
+}
+
+// 8 codes of one column (bits [sh, sh + 8·BITS) of hi:lo) → 8 bf16 Ŵ
+// (nb = −128·s, exact).
+template <int BITS>
+__device__ __forceinline__ bf16x8_t dq_chunk(uint32_t lo, uint32_t hi, uint32_t sh, float s,
+                                             float nb, uint32_t z) {
+  bf16x8_t b;
+  if constexpr (BITS == 4) {
+    const uint32_t L = (lo & 0x0F0F0F0Fu) + z, H = ((lo >> 4) & 0x0F0F0F0Fu) + z;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      b[2 * p] = (__bf16)fmaf((float)((L >> (8 * p)) & 0xFFu), s, nb);
+      b[2 * p + 1] = (__bf16)fmaf((float)((H >> (8 * p)) & 0xFFu), s, nb);
+    }
+  } else if constexpr (BITS == 8) {
+    const float zf = __uint_as_float(z);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      b[p] = (__bf16)(s * ((float)((lo >> (8 * p)) & 0xFFu) - zf));
+      b[4 + p] = (__bf16)(s * ((float)((hi >> (8 * p)) & 0xFFu) - zf));
+    }
+  } else {
+    const uint32_t v = (uint32_t)((((uint64_t)hi << 32) | lo) >> sh);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      b[i] = (__bf16)fmaf((float)(__builtin_amdgcn_ubfe(v, i * BITS, BITS) + z), s, nb);
   }
-  __syncthreads();
-  float acc[MT];
+  return b;
+}
+
+// Four adjacent words at columns col .. col + 3 of packed row p + r·N (VEC:
+// one 16-byte load, N % 4 == 0 and all four in range; else per column, zero
+// past N).
+template <bool VEC>
+__device__ __forceinline__ u32x4_t load_cols(const uint32_t* p, uint32_t r, int N, int col) {
+  if constexpr (VEC) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + r * (uint32_t)N + col));
+  } else {
+    u32x4_t v = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-  if (n < N) {
-    const uint32_t nwords = (uint32_t)(K * BITS / 32);
-    const int g8 = a.g / 8;                       // chunks per group
-    const uint32_t zw = (uint32_t)((int64_t)N * BITS / 32);
-    for (int c0 = wave; c0 < nc; c0 += 4 * GEMV_BATCH) {
-      uint32_t lo[GEMV_BATCH], hi[GEMV_BATCH], zlo[GEMV_BATCH], zhi[GEMV_BATCH];
-      float sc[GEMV_BATCH];
+    for (int i = 0; i < 4; ++i)
+      if (col + i < N) v[i] = p[r * (uint32_t)N + col + i];
+    return v;
+  }
+}
+
+// Steps of 32 k whose packed words are loaded together: two such batches are
+// in flight per wave (the next one is loaded while the current one is used).
+template <int BITS>
+__host__ __device__ constexpr int dq_batch() { return BITS == 4 ? 8 : BITS == 3 ? 2 : 4; }
+
+// Slice k0 .. k0 + Lk of K (Lk % 32 == 0, Lk <= DQ_MAX_LK; the last slice
+// ends at K), computed as whole batches over Lp = Lk rounded up to 32·B.
+// LDS: X rows [M][Lp + 8] bf16, zero from the slice's end; scale, −128·scale
+// and zero-point term [groups][DQ_GSTRIDE]; the group-row offset of each
+// chunk [Lp / 8].
+template <int BITS, bool VEC>
+__global__ __launch_bounds__(NT, 4) void k_dq_mfma(   // at most 128 VGPRs: 4 waves per SIMD
+DqArgs a, const uint16_t* X, int M, float* part,
+                                                int Lk) {
+  constexpr int B = dq_batch<BITS>();
+  extern __shared__ __attribute__((aligned(16))) uint8_t dq_lds[];
+  const int N = (int)a.N, K = (int)a.K, g = a.g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cb = blockIdx.x * DQ_COLS;
+  const int k0 = blockIdx.y * Lk, k1 = min(k0 + Lk, K);
+  const int Lp = (Lk + 32 * B - 1) / (32 * B) * (32 * B);
+  const int j0 = k0 / g, ng = (k1 - 1) / g - j0 + 1;
+  const int xstride = Lp + 8;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(dq_lds);
+  float* gs = reinterpret_cast<float*>(dq_lds + ((M * xstride * 2 + 15) & ~15));
+  float* gn = gs + ng * DQ_GSTRIDE;
+  uint32_t* gz = reinterpret_cast<uint32_t*>(gn + ng * DQ_GSTRIDE);
+  int* grow = reinterpret_cast<int*>(gz + ng * DQ_GSTRIDE);
+
+  const int lcol = 64 * wave + 4 * (lane & 15);   // first of the lane's columns in the workgroup
+  const int col = cb + lcol;
+  const int q = lane >> 4;
+  const bool live = col < N;   // columns past N: words read as 0, s = 0, so B = 0
+  // Step t reads packed word w0 + t·BITS of each column at the same bit offset
+  // (32 codes are 32·BITS bits = BITS words).
+  const uint32_t off0 = (uint32_t)(k0 + 8 * q) * BITS, sh = off0 & 31;
+  // the chunk reaches into the next word: never at 2 and 4 bits, always at 8
+  const bool two = BITS == 8 || (BITS == 3 && sh + 8 * BITS > 32);
+  // Chunks past the slice meet X = 0, so any finite B will do there: their
+  // loads are redirected to the lane's last chunk inside K (to row 0 if it has
+  // none), and columns past N (their s is 0) to the last four columns. Inside
+  // K the chunk's bits end inside the packed column (k + 8 <= K), so a second
+  // word exists when it is read.
+  const bool has = k0 + 8 * q + 8 <= K;
+  const int tmax = has ? (K - k0 - 8 * q - 8) / 32 : 0;
+  const uint32_t* qcol = a.qw + (has ? off0 >> 5 : 0u) * (uint32_t)N;
+  const int colc = VEC ? (live ? col : N - 4) : col;
+  auto issue = [&](int b, u32x4_t (&lo)[B], u32x4_t (&hi)[B]) {
 #pragma unroll
-      for (int u = 0; u < GEMV_BATCH; ++u) {
-        const int c = c0 + 4 * u;
-        if (c < nc) {
-          const uint32_t off = (uint32_t)(c_begin + c) * (8 * BITS);
-          const uint32_t w = off >> 5, sh = off & 31;
-          lo[u] = a.qw[w * (uint32_t)N + n];
-          hi[u] = (sh + 8 * BITS > 32 && w + 1 < nwords) ? a.qw[(w + 1) * (uint32_t)N + n] : 0u;
-          const uint32_t j = (uint32_t)(c_begin + c) / (uint32_t)g8;
-          sc[u] = a.scale[(uint32_t)n * (uint32_t)a.G + j];
-          if (a.qz) {
-            const uint32_t zo = (uint32_t)n * BITS, zwi = zo >> 5;
-            zlo[u] = a.qz[j * zw + zwi];
-            zhi[u] = ((zo & 31) + BITS > 32 && zwi + 1 < zw) ? a.qz[j * zw + zwi + 1] : 0u;
-          }
-        }
+    for (int u = 0; u < B; ++u) {
+      const int t = min(b * B + u, tmax);
+      const uint32_t* p = qcol + (uint32_t)(t * BITS) * (uint32_t)N;
+      lo[u] = load_cols<VEC>(p, 0, N, colc);
+      if constexpr (BITS == 8) {
+        hi[u] = load_cols<VEC>(p, 1, N, colc);
+      } else if constexpr (BITS == 3) {
+        hi[u] = u32x4_t{0u, 0u, 0u, 0u};
+        if (two) hi[u] = load_cols<VEC>(p, 1, N, colc);
+      } else {
+        hi[u] = lo[u];   // unused
       }
+    }
+  };
+  u32x4_t la[B], ha[B], lb[B], hb[B];
+  issue(0, la, ha);   // in flight while the workgroup stages its LDS
+
+  // X slice, zero from the slice's end (K % 8 == 0: a chunk is wholly in or out).
+  const int cx = Lp / 8;
+  for (int i = threadIdx.x; i < M * cx; i += NT) {
+    const int m = i / cx, c = i - m * cx, k = k0 + 8 * c;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (k < k1) v = *reinterpret_cast<const u32x4_t*>(X + (int64_t)m * K + k);
+    *reinterpret_cast<u32x4_t*>(xs + m * xstride + 8 * c) = v;
+  }
+  // Scale and zero-point term of each (group, column); columns past N get s = 0.
+  for (int i = threadIdx.x; i < ng * DQ_COLS; i += NT) {
+    const int cl = i / ng, jj = i - cl * ng, n = cb + cl, j = j0 + jj;
+    float sv = 0.0f;
+    uint32_t zp = 1u << (BITS - 1);
+    if (n < N) {
+      sv = a.scale[(uint32_t)n * (uint32_t)a.G + j];
+      if (a.qz) {
+        const uint32_t zw = (uint32_t)(N * BITS / 32), zo = (uint32_t)n * BITS, zi = zo >> 5;
+        uint64_t v = a.qz[j * zw + zi];
+        if ((zo & 31) + BITS > 32) v |= (uint64_t)a.qz[j * zw + zi + 1] << 32;
+        zp = (uint32_t)(v >> (zo & 31)) & ((1u << BITS) - 1u);
+      }
+    }
+    gs[jj * DQ_GSTRIDE + cl] = sv;
+    gn[jj * DQ_GSTRIDE + cl] = -128.0f * sv;
+    gz[jj * DQ_GSTRIDE + cl] = zp_term<BITS>(zp);
+  }
+  // Chunk c of the slice (k = k0 + 8c; past the slice: its last group) → group row.
+  for (int c = threadIdx.x; c < Lp / 8; c += NT)
+    grow[c] = (min(k0 + 8 * c, k1 - 1) / g - j0) * DQ_GSTRIDE;
+  __syncthreads();
+
+  const uint16_t* xrow = xs + min(lane & 15, M - 1) * xstride + 8 * q;
+  f32x4_t acc[4];
 #pragma unroll
-      for (int u = 0; u < GEMV_BATCH; ++u) {
-        const int c = c0 + 4 * u;
-        if (c < nc) {
-          const uint32_t sh = ((uint32_t)(c_begin + c) * (8 * BITS)) & 31;
-          const uint64_t v = ((uint64_t)hi[u] << 32 | lo[u]) >> sh;
-          float zp;
-          if (a.qz) {
-            const uint32_t zs = ((uint32_t)n * BITS) & 31;
-            zp = (float)((uint32_t)(((uint64_t)zhi[u] << 32 | zlo[u]) >> zs) & MASK);
-          } else {
-            zp = (float)(1 << (BITS - 1));
-          }
-          float w[8];
-          dequant_bits<BITS>(v, zp, sc[u], w);
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](int b, const u32x4_t (&lo)[B], const u32x4_t (&hi)[B]) {
 #pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            if (MT == 1 || m < M) {
-              float x[8];
-              load8(xs + (m * nc + c) * 8, x);
+    for (int u = 0; u < B; ++u) {
+      const int t = b * B + u;
+      const int go = grow[4 * t + q];
+      const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(gs + go + lcol);
+      const f32x4_t nv = *reinterpret_cast<const f32x4_t*>(gn + go + lcol);
+      const u32x4_t zv = *reinterpret_cast<const u32x4_t*>(gz + go + lcol);
+      const bf16x8_t xa = *reinterpret_cast<const bf16x8_t*>(xrow + 32 * t);
 #pragma unroll
-              for (int i = 0; i < 8; ++i) acc[m] = fmaf(x[i], w[i], acc[m]);
-            }
-          }
+      for (int i = 0; i < 4; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            xa, dq_chunk<BITS>(lo[u][i], hi[u][i], sh, sv[i], nv[i], zv[i]), acc[i], 0, 0, 0);
+    }
+  };
+  // Batches alternate between the two register sets; the loop leaves only
+  // after a whole batch, so no branch separates the MFMAs of one.
+  const int nb = ((k1 - k0 + 31) / 32 + B - 1) / B;
+  for (int b = 0;;) {
+    if (b + 1 < nb) issue(b + 1, lb, hb);
+    compute(b, la, ha);
+    if (++b == nb) break;
+    if (b + 1 < nb) issue(b + 1, la, ha);
+    compute(b, lb, hb);
+    if (++b == nb) break;
+  }
+  // Output rows 4·(l / 16) + r of the lane's columns.
+  if (live) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = 4 * q + r;
+      if (m < M) {
+        float* dst = part + ((int64_t)blockIdx.y * M + m) * N + col;
+        if constexpr (VEC) {
+          *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (col + i < N) dst[i] = acc[i][r];
         }
       }
     }
   }
-#pragma unroll
-  for (int m = 0; m < MT; ++m)
-    if (m < M) red[wave][m][lane] = acc[m];
-  __syncthreads();
-  for (int t = threadIdx.x; t < M * GEMV_COLS; t += NT) {
-    const int m = t / GEMV_COLS, l = t % GEMV_COLS;
-    const int64_t nn = (int64_t)blockIdx.x * GEMV_COLS + l;
-    if (nn < a.N)
-      part[((int64_t)blockIdx.y * M + m) * a.N + nn] =
-          ((red[0][m][l] + red[1][m][l]) + red[2][m][l]) + red[3][m][l];
-  }
 }
 
-// Y[m, n] = sum over slices, in slice order.
+// Y[m, n] = sum over slices, in slice order; the partials of up to 8 slices
+// are loaded together before they are added.
 __global__ __launch_bounds__(NT) void k_dq_reduce(const float* part, int S, int64_t MN, void* Y,
                                                   int ydt) {
   for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < MN; i += (int64_t)gridDim.x * NT) {
     float s = 0.0f;
-    for (int k = 0; k < S; ++k) s += part[(int64_t)k * MN + i];
+    for (int k0 = 0; k0 < S; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = k0 + u < S ? part[(int64_t)(k0 + u) * MN + i] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < S) s += v[u];
+    }
     if (ydt == AR_BF16)
       static_cast<uint16_t*>(Y)[i] = (uint16_t)bf16_bits(s);
     else
@@ -215,22 +353,118 @@ ar_status dq_blocked(const DqArgs& a, uint16_t* WB, int64_t nkb, hipStream_t st)
   return last_status();
 }
 
-template <int BITS, int MT>
-ar_status dq_gemv_m(const DqArgs& a, const uint16_t* X, int M, float* part, int S, int cps,
-                    hipStream_t st) {
-  const dim3 grid((unsigned)((a.N + GEMV_COLS - 1) / GEMV_COLS), (unsigned)S);
-  hipLaunchKernelGGL((k_dq_gemv<BITS, MT>), grid, dim3(NT), 0, st, a, X, M, part, cps);
-  return last_status();
+struct DqPlan {
+  int S, Lk;
+  size_t lds;
+};
+
+template <int BITS>
+const void* dq_kernel(bool vec) {
+  return vec ? reinterpret_cast<const void*>(&k_dq_mfma<BITS, true>)
+             : reinterpret_cast<const void*>(&k_dq_mfma<BITS, false>);
+}
+
+// Workgroups of the small-M kernel resident at once on the current device with
+// `lds` bytes of LDS each (a fixed guess if the runtime cannot say); the
+// answers are remembered per device, bit width, load form and LDS size.
+int dq_capacity(int bits, bool vec, size_t lds) {
+  struct Entry {
+    int dev, bits, vec;
+    size_t lds;
+    int cap;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> seen;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256 * 3;
+  }
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    for (const Entry& e : seen)
+      if (e.dev == dev && e.bits == bits && e.vec == (int)vec && e.lds == lds) return e.cap;
+  }
+  const void* f = bits == 2 ? dq_kernel<2>(vec) : bits == 3 ? dq_kernel<3>(vec)
+                : bits == 4 ? dq_kernel<4>(vec) : dq_kernel<8>(vec);
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, f, NT, lds) != hipSuccess ||
+      cus <= 0 || per <= 0) {
+    (void)hipGetLastError();
+    return 256 * 3;
+  }
+  std::lock_guard<std::mutex> lk(mu);
+  if (seen.size() < 4096) seen.push_back(Entry{dev, bits, (int)vec, lds, cus * per});
+  return cus * per;
+}
+
+size_t dq_lds_bytes(int64_t M, int64_t Lp, int64_t L, int64_t g, int64_t K) {
+  const int64_t G = K / g;
+  int64_t ng = (L - 1) / g + 2;   // groups a slice of L can touch
+  if (ng > G) ng = G;
+  return (size_t)((M * (Lp + 8) * 2 + 15) / 16 * 16 + ng * DQ_GSTRIDE * 12 + Lp / 8 * 4);
+}
+
+// Slices of the small-M product. Lk is a multiple of 32 no longer than the X
+// budget (M rows), the group budget and DQ_MAX_LK allow; the kernel runs
+// whole batches of 32·B, so a slice costs its length rounded up to that, plus
+// DQ_WG_COST, plus its partial sums. Among slice counts, the one with the least
+// (waves of resident workgroups) x (cost of a slice) wins, the fewest slices
+// on ties.
+DqPlan dq_plan(int bits, bool vec, int64_t N, int64_t K, int64_t M, int64_t g) {
+  const int64_t unit = 32 * (bits == 4 ? 8 : bits == 3 ? 2 : 4);
+  const int64_t colblocks = (N + DQ_COLS - 1) / DQ_COLS;
+  const int64_t Mr = M > 0 ? M : 1;
+  const int64_t Kr = (K + 31) / 32 * 32;
+  const int64_t Lx = (DQ_X_LDS / Mr / 2 - 8) / 32 * 32;
+  const int64_t maxg = DQ_G_LDS / (DQ_GSTRIDE * 12);                // group rows that fit
+  const int64_t Lg = g >= K ? Kr : (maxg - 2) * g / 32 * 32;          // slice touches <= L/g + 2
+  int64_t Lmax = Kr < DQ_MAX_LK ? Kr : DQ_MAX_LK;
+  if (Lx < Lmax) Lmax = Lx;
+  if (Lg < Lmax) Lmax = Lg;
+  if (Lmax < 32) Lmax = 32;
+  DqPlan best{0, 0, 0};
+  int64_t best_cost = -1;
+  int cap = -1;
+  size_t cap_lds = 0;
+  for (int64_t s = (K + Lmax - 1) / Lmax; s <= (K + 31) / 32; ++s) {
+    int64_t L = ((K + s - 1) / s + 31) / 32 * 32;
+    if (L >= unit && L % unit != 0) {   // whole batches when the budget allows
+      const int64_t Lu = (L + unit - 1) / unit * unit;
+      if (Lu <= Lmax) L = Lu;
+    }
+    if (L > Lmax) continue;
+    const int64_t S = (K + L - 1) / L;
+    if (S != s) continue;               // the same plan as a smaller count
+    const int64_t Lp = (L + unit - 1) / unit * unit;
+    const size_t lds = dq_lds_bytes(Mr, Lp, L, g, K);
+    if (cap < 0 || lds != cap_lds) {
+      cap = dq_capacity(bits, vec, lds);
+      cap_lds = lds;
+    }
+    // the slice's partial sums (written, then read by the reduction) cost as
+    // many HBM bytes as 64·M/BITS k of packed words
+    const int64_t waves = (colblocks * S + cap - 1) / cap;
+    const int64_t cost = waves * (Lp + DQ_WG_COST + (S > 1 ? 64 * Mr / bits : 0));
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = DqPlan{(int)S, (int)L, lds};
+    }
+    if (L <= 32) break;
+  }
+  return best;
 }
 
 template <int BITS>
-ar_status dq_gemv(const DqArgs& a, const uint16_t* X, int M, float* part, int S, int cps,
-                  hipStream_t st) {
-  if (M <= 1) return dq_gemv_m<BITS, 1>(a, X, M, part, S, cps, st);
-  if (M <= 2) return dq_gemv_m<BITS, 2>(a, X, M, part, S, cps, st);
-  if (M <= 4) return dq_gemv_m<BITS, 4>(a, X, M, part, S, cps, st);
-  if (M <= 8) return dq_gemv_m<BITS, 8>(a, X, M, part, S, cps, st);
-  return dq_gemv_m<BITS, 16>(a, X, M, part, S, cps, st);
+ar_status dq_small(const DqArgs& a, const uint16_t* X, int M, float* part, const DqPlan& p,
+                   bool vec, hipStream_t st) {
+  const dim3 grid((unsigned)((a.N + DQ_COLS - 1) / DQ_COLS), (unsigned)p.S);
+  if (vec)
+    hipLaunchKernelGGL((k_dq_mfma<BITS, true>), grid, dim3(NT), p.lds, st, a, X, M, part, p.Lk);
+  else
+    hipLaunchKernelGGL((k_dq_mfma<BITS, false>), grid, dim3(NT), p.lds, st, a, X, M, part, p.Lk);
+  return last_status();
 }
 
 DqArgs dq_args(const int32_t* qweight, const int32_t* qzeros, const float* scale, int64_t N,
@@ -248,22 +482,13 @@ DqArgs dq_args(const int32_t* qweight, const int32_t* qzeros, const float* scale
 
 }  // namespace
 
-// Row bucket of the small-M product.
-static int gemv_bucket(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
+// 16-byte packed-word loads need N % 4 == 0 and an aligned qweight.
+static bool dq_vec(const int32_t* qweight, int64_t N) {
+  return N % 4 == 0 && (reinterpret_cast<uintptr_t>(qweight) & 15) == 0;
+}
 
-// Slices of the small-M product: about two workgroups per CU, at least 16
-// chunks of 8 codes per slice, and few enough chunks that the X slice fits
-// the bucket's LDS stage.
-int ar_dq_slices(int64_t N, int64_t K, int64_t M) {
-  const int64_t colblocks = (N + GEMV_COLS - 1) / GEMV_COLS;
-  const int64_t chunks = K / 8;
-  int64_t S = (512 + colblocks - 1) / colblocks;
-  const int64_t maxS = chunks / 16;
-  if (S > maxS) S = maxS;
-  if (S < 1) S = 1;
-  const int64_t max_cps = gemv_xlds(gemv_bucket(M)) / (16 * (M > 0 ? M : 1));
-  while ((chunks + S - 1) / S > max_cps) ++S;
-  return (int)S;
+int ar_dq_slices(int bits, int64_t N, int64_t K, int64_t M, int64_t g) {
+  return dq_plan(bits, N % 4 == 0, N, K, M, g).S;
 }
 
 ar_status ar_launch_dequant_blocked(int bits, const int32_t* qweight, const int32_t* qzeros,
@@ -284,21 +509,20 @@ ar_status ar_launch_dq_gemv(int bits, const int32_t* qweight, const int32_t* qze
                             const float* scale, int64_t N, int64_t K, int g, const uint16_t* X,
                             int M, float* part, void* Y, int ydt, hipStream_t st) {
   const DqArgs a = dq_args(qweight, qzeros, scale, N, K, g);
-  const int S = ar_dq_slices(N, K, M);
-  const int64_t chunks = K / 8;
-  const int cps = (int)((chunks + S - 1) / S);
+  const bool vec = dq_vec(qweight, N);
+  const DqPlan p = dq_plan(bits, N % 4 == 0, N, K, M, g);   // as the workspace size assumed
   ar_status s;
   switch (bits) {
-    case 2: s = dq_gemv<2>(a, X, M, part, S, cps, st); break;
-    case 3: s = dq_gemv<3>(a, X, M, part, S, cps, st); break;
-    case 4: s = dq_gemv<4>(a, X, M, part, S, cps, st); break;
-    case 8: s = dq_gemv<8>(a, X, M, part, S, cps, st); break;
+    case 2: s = dq_small<2>(a, X, M, part, p, vec, st); break;
+    case 3: s = dq_small<3>(a, X, M, part, p, vec, st); break;
+    case 4: s = dq_small<4>(a, X, M, part, p, vec, st); break;
+    case 8: s = dq_small<8>(a, X, M, part, p, vec, st); break;
     default: return AR_ERR_UNSUPPORTED;
   }
   if (s != AR_OK) return s;
   const int64_t MN = (int64_t)M * N;
   const int64_t nb = (MN + NT - 1) / NT;
   hipLaunchKernelGGL(k_dq_reduce, dim3((unsigned)(nb < 65536 ? nb : 65536)), dim3(NT), 0, st, part,
-                     S, MN, Y, ydt);
+                     p.S, MN, Y, ydt);
   return last_status();
 }

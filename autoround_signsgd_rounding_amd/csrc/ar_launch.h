@@ -117,7 +117,7 @@ ar_status ar_launch_dequant_blocked(int bits, const int32_t* qweight, const int3
                                     const float* scale, int64_t N, int64_t K, int g, uint16_t* WB,
                                     hipStream_t st);
 // Split-K slices of the small-M product; its workspace is slices*M*N floats.
-int ar_dq_slices(int64_t N, int64_t K, int64_t M);
+int ar_dq_slices(int bits, int64_t N, int64_t K, int64_t M, int64_t g);
 // Y[M, N] = X·bf16(Ŵ)ᵀ for M <= 16.
 ar_status ar_launch_dq_gemv(int bits, const int32_t* qweight, const int32_t* qzeros,
                             const float* scale, int64_t N, int64_t K, int g, const uint16_t* X,

@@ -108,8 +108,8 @@ def _dequant_run(ar, torch, X, out, w, reps=20):
     for M in (1, 16, w.Tb):
         Xm = X[:M]
         Yo = torch.empty((M, w.N), dtype=torch.float32, device=X.device)
-        ws = torch.empty(max(ar.dequant_gemm_workspace_size(w.bits, M, w.N, w.K), 256),
-                         dtype=torch.uint8, device=X.device)
+        need = ar.dequant_gemm_workspace_size(w.bits, w.group_size, M, w.N, w.K)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
 
         def call():
             ar.dequant_gemm(Xm, qw, qz, out.scale, w.bits, w.group_size, w.N, out=Yo,
@@ -174,7 +174,7 @@ def _decode_large(ar, torch, reps, N=29568, K=8192, bits=4, g=128):
     sc = torch.rand((N, G), device=dev, generator=gen) * 0.01
     X = torch.randn((1, K), device=dev, generator=gen).to(torch.bfloat16)
     Y = torch.empty((1, N), device=dev)
-    ws = torch.empty(max(ar.dequant_gemm_workspace_size(bits, 1, N, K), 256), dtype=torch.uint8,
+    ws = torch.empty(max(ar.dequant_gemm_workspace_size(bits, g, 1, N, K), 256), dtype=torch.uint8,
                      device=dev)
 
     def call():

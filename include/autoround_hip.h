@@ -197,11 +197,14 @@ ar_status ar_tune_linear(const ar_config* cfg, int32_t wdt, const void* W, int64
    zp = 2^(bits-1)); scale [N, G] float32 (ar_tune_linear's layout); Y [M, N]
    row-major, ydt AR_F32 or AR_BF16. float32 accumulation. group_size as in
    ar_config (-1: whole row); K*bits % 32 == 0, K % group = 0, group % 8 == 0;
-   with qzeros N*bits % 32 == 0. M <= 16 reads the packed words directly
-   (split-K, slices summed in a fixed order); larger M dequantizes once into a
-   blocked bf16 operand and runs the MFMA product. M = 0 or N = 0 is a no-op. */
-ar_status ar_dequant_gemm_workspace_size(int32_t bits, int64_t M, int64_t N, int64_t K,
-                                         size_t* bytes);
+   with qzeros N*bits % 32 == 0. M <= 16 streams the packed words once,
+   dequantizing each code once for all M rows (split-K, slices summed in a fixed
+   order); larger M dequantizes once into a blocked bf16 operand and runs the
+   MFMA product. M = 0 or N = 0 is a no-op. The workspace size depends on bits,
+   group_size and the shape (the split-K slice length follows the group size);
+   ar_dequant_gemm_workspace_size validates them as ar_dequant_gemm does. */
+ar_status ar_dequant_gemm_workspace_size(int32_t bits, int32_t group_size, int64_t M, int64_t N,
+                                         int64_t K, size_t* bytes);
 ar_status ar_dequant_gemm(int32_t bits, int32_t group_size, const uint16_t* X, int64_t M,
                           int64_t K, const int32_t* qweight, const int32_t* qzeros,
                           const float* scale, int64_t N, void* Y, int32_t ydt, void* ws,

@@ -537,8 +537,8 @@ def dequantize(qweight, qzeros, scale, bits: int, group_size: int, N: int, K: in
     2^(bits-1) when qzeros is None, the symmetric grid), scale [N, G] float32,
     then s·(q - zp) in float32."""
     g = K if group_size == -1 else group_size
-    if qzeros is None:
-        codes, _ = unpack(qweight, np.zeros((1, N * bits // 32), np.uint32), bits, N, K)
+    if qzeros is None:   # symmetric grid: no zero-point words, N need not fill words
+        codes = _unpack_axis0(qweight, bits, K).T.copy()
         zp = np.full((N, K // g), 2 ** (bits - 1), np.int64)
     else:
         codes, zp = unpack(qweight, qzeros, bits, N, K)

@@ -22,9 +22,10 @@ def _packed(N, K, bits, g, sym, seed):
     codes = rng.integers(0, 2 ** bits, (N, K), dtype=np.uint8)
     zp = rng.integers(0, 2 ** bits, (N, G), dtype=np.uint8)
     scale = (rng.uniform(0.5, 2.0, (N, G)) * 0.01).astype(F32)
+    if sym:   # no zero-points: pack placeholder ones for a whole number of words
+        qw, _ = O.pack(codes, np.zeros((-(-N // 32) * 32, G), np.uint8), bits)
+        return qw, None, scale
     qw, qz = O.pack(codes, zp, bits)
-    if sym:
-        qz = None
     return qw, qz, scale
 
 
@@ -42,6 +43,13 @@ CASES = [
     (300, 520, 200, 8, 40, False, "f32"),     # ragged tiles and reduction
     (257, 128, 768, 3, 96, False, "bf16"),
     (64, 160, 256, 2, -1, False, "f32"),
+    # small-M path: columns not a multiple of 4 (per-column loads), groups of
+    # 24 and 8 (several groups per 32-wide step), a K tail past the last step
+    (2, 90, 256, 4, 64, True, "f32"),
+    (4, 128, 384, 3, 24, False, "f32"),
+    (1, 256, 256, 2, 8, False, "f32"),
+    (7, 520, 200, 8, 40, False, "f32"),
+    (16, 300, 1024, 4, -1, True, "bf16"),
 ]
 
 
@@ -115,7 +123,7 @@ def test_decode_product_under_graph_capture():
     args = (_gpu_i32(qw), _gpu_i32(qz), torch.from_numpy(scale).to(dev()), 4, 128, N)
     eager = ar.dequant_gemm(Xd, *args)
     Y = torch.empty_like(eager)
-    ws = torch.empty(max(ar.dequant_gemm_workspace_size(4, M, N, K), 256), dtype=torch.uint8,
+    ws = torch.empty(max(ar.dequant_gemm_workspace_size(4, 128, M, N, K), 256), dtype=torch.uint8,
                      device=dev())
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -132,3 +140,38 @@ def test_decode_product_under_graph_capture():
         junk = ar.dequant_gemm(Xd[:1], *args)          # eager work between replays
         torch.cuda.synchronize()
         del junk
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_full_size_sampled_columns(bits, M):
+    """The decode sizes on a Qwen2.5-72B up_proj-shaped layer (8192 -> 29568,
+    g128 asym, random packed words: every word is a valid packing), in the
+    launch configuration the product uses at this size (several 32-wide steps
+    per slice, a half-filled last column block). Aligned blocks of 32 columns
+    are sampled: their qweight columns, qzeros words and scale rows form a
+    32-column layer of their own, which the oracle multiplies."""
+    N, K, g = 29568, 8192, 128
+    G = K // g
+    log(f"dequant_gemm full size M={M} b{bits}: generating")
+    gen = torch.Generator(device=dev())
+    gen.manual_seed(bits * 100 + M)
+    qw = torch.randint(-2 ** 31, 2 ** 31 - 1, (K * bits // 32, N), dtype=torch.int32,
+                       device=dev(), generator=gen)
+    qz = torch.randint(-2 ** 31, 2 ** 31 - 1, (G, N * bits // 32), dtype=torch.int32,
+                       device=dev(), generator=gen)
+    scale = (torch.rand((N, G), device=dev(), generator=gen) + 0.5) * 0.01
+    X = torch.randn((M, K), device=dev(), generator=gen).to(torch.bfloat16)
+    Y = ar.dequant_gemm(X, qw, qz, scale, bits, g, N)
+    torch.cuda.synchronize()
+    Xf = X.float().cpu().numpy()
+    got = to_np(Y).astype(np.float64)
+    qw_h, qz_h, sc_h = (to_np(t) for t in (qw, qz, scale))
+    for c0 in (0, 256 * 57 + 96, N - 256 - 32, N - 32):
+        zc = slice(c0 * bits // 32, (c0 + 32) * bits // 32)
+        ref = O.dequant_matmul(Xf, qw_h[:, c0:c0 + 32].view(np.uint32),
+                               qz_h[:, zc].view(np.uint32), sc_h[c0:c0 + 32], bits, g, 32, K)
+        err = rel_norm(got[:, c0:c0 + 32], ref)
+        log(f"  columns {c0}..{c0 + 31}: rel err {err:.2e}")
+        assert err <= 1e-5
+        assert np.abs(got[:, c0:c0 + 32] - ref).max() <= 1e-5 * np.abs(ref).max()

@@ -610,3 +610,22 @@ def test_dequant_matmul_hand_example():
     Y = O.dequant_matmul(X, qw, qz, scale, 4, 8, 8, 8)
     np.testing.assert_allclose(Y[0, :2], [2.5, 1.75])
     assert not Y[0, 2:].any()
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_aligned_column_block_is_a_packed_layer(bits):
+    """32 adjacent columns starting at a multiple of 32 are a packed layer of
+    their own: their qweight columns, the qzeros words that hold their
+    zero-points and their scale rows dequantize to the same Ŵ rows as the whole
+    layer (the large-shape GPU tests compare such blocks)."""
+    rng = np.random.default_rng(70 + bits)
+    N, K, g = 96, 256, 64
+    codes = rng.integers(0, 2 ** bits, (N, K), dtype=np.uint8)
+    zp = rng.integers(0, 2 ** bits, (N, K // g), dtype=np.uint8)
+    scale = rng.uniform(0.5, 2.0, (N, K // g)).astype(F32)
+    qw, qz = O.pack(codes, zp, bits)
+    full = O.dequantize(qw, qz, scale, bits, g, N, K)
+    for c0 in (0, 32, 64):
+        zc = slice(c0 * bits // 32, (c0 + 32) * bits // 32)
+        sub = O.dequantize(qw[:, c0:c0 + 32], qz[:, zc], scale[c0:c0 + 32], bits, g, 32, K)
+        np.testing.assert_array_equal(sub, full[c0:c0 + 32])
