@@ -29,7 +29,7 @@ EXPORTS = (
     "ar_gram_workspace_size", "ar_gram_step_workspace_size", "ar_tune_step_gram",
     "ar_tune_linear_gram", "ar_init_clip", "ar_resolve_layer_config", "ar_resolve_fused_config",
     "ar_dequant_gemm_workspace_size", "ar_dequant_gemm", "ar_block_workspace_size",
-    "ar_block_forward", "ar_tune_block",
+    "ar_block_forward", "ar_tune_block", "ar_attention",
 )
 
 
@@ -132,6 +132,7 @@ def _load():
         "ar_block_workspace_size": [cfgp, ctypes.POINTER(ArBlockDims), ctypes.POINTER(sz)],
         "ar_block_forward": [ctypes.POINTER(ArBlockDims), ctypes.POINTER(ArBlockWeights), vp, vp,
                              vp, sz, vp],
+        "ar_attention": [ctypes.POINTER(ArBlockDims), vp, vp, vp, vp, vp],
         "ar_tune_block": [cfgp, ctypes.POINTER(ArBlockDims), ctypes.POINTER(ArBlockWeights), vp,
                           vp, i32, ctypes.POINTER(ArBlockOutputs), vp, sz, vp],
         "ar_pack": [i32, vp, vp, i64, i64, i64, vp, vp, vp],
@@ -509,6 +510,18 @@ def block_forward(h, W: dict, norms, dims: ArBlockDims, stream=None):
     out = torch.empty_like(h)
     _check(lib.ar_block_forward(ctypes.byref(dims), ctypes.byref(bw), _ptr(h), _ptr(out),
                                 _ptr(ws), ws.numel(), _stream(stream)), "ar_block_forward")
+    return out
+
+
+def attention(q, k, v, dims: ArBlockDims, out=None, stream=None):
+    """The block's causal attention step (ar_attention) on rotated q, k and v
+    [nsamples·seqlen, hidden] bf16; returns out of the same shape."""
+    torch = _torch()
+    _dev(q, k, v, out)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.ar_attention(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                            _stream(stream)), "ar_attention")
     return out
 
 

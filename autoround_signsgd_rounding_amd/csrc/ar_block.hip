@@ -12,7 +12,8 @@
 // Activations are bf16 between operations. Each operation rounds its float32
 // result to bf16 (RNE): RMSNorm sums squares in float64, the rotary table is
 // float64 rounded to float32, SiLU·mul is float64, additions float32, the
-// Linears float32 MFMA accumulation, attention float32 with an online softmax.
+// Linears float32 MFMA accumulation, attention float32 MFMA accumulation with
+// an online softmax.
 #include <math.h>
 #include <string.h>
 
@@ -101,72 +102,139 @@ __global__ __launch_bounds__(NT) void k_add(const uint16_t* a, const uint16_t* b
 }
 
 // ------------------------------------------------------------------ attention
-// Causal attention for one (sequence, head) and 256 queries per workgroup, one
-// query per thread: keys and values go through LDS in tiles of KT; per tile
-// the scores are formed first, then the running max, the rescale of the
-// running sums, and the weighted values (online softmax, float32).
+// Causal attention on v_mfma_f32_16x16x32_bf16, for one (sequence, head) and
+// 64 queries per workgroup (16 per wave). Keys and values pass through LDS in
+// tiles of 64: K row-major, V transposed (Vᵀ[dh][key]).
+//
+// Scores are formed transposed, Sᵀ = K·Qᵀ (A: 8 dh of a key row, B: the same
+// 8 dh of a query), so lane l holds query l % 16 at keys 16j + 4·(l/16) + r of
+// the tile. The online softmax therefore keeps one running max and sum per
+// lane, exchanged across the four lanes of a query only for the tile max and
+// the final sum. P = exp(s − max) is split into three bf16 parts whose sum is
+// the float32 weight to its last bit or so, and Oᵀ = Vᵀ·Pᵀ takes each part as
+// the B operand in the same registers it was computed in; the A operand reads
+// Vᵀ at the lane's keys.
+// Float32 throughout; exp is exp2 of scores pre-scaled by log2(e)/sqrt(Dh).
 template <int DH>
 __global__ __launch_bounds__(NT) void k_attention(const uint16_t* __restrict__ q,
                                                   const uint16_t* __restrict__ k,
                                                   const uint16_t* __restrict__ v,
                                                   uint16_t* __restrict__ out, int D, int S,
-                                                  int H, float scale) {
-  constexpr int KT = 32;
-  __shared__ float ks[KT][DH];
-  __shared__ float vs[KT][DH];
+                                                  int H, float scale_log2e) {
+  constexpr int KT = 64;            // keys per tile
+  constexpr int KS = DH + 8;        // K row stride (elements): rows 16 banks apart
+  constexpr int VS = KT + 8;        // Vᵀ row stride (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t ks[KT * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[DH * VS];
   const int b = blockIdx.x / H, h = blockIdx.x % H;
-  const int q0 = blockIdx.y * NT;
-  const int i = q0 + threadIdx.x;
-  const bool live = i < S;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g4 = lane >> 4;
+  const int qb = blockIdx.y * 64;          // first query of the workgroup
+  const int qw = qb + 16 * wave;           // first query of the wave
+  const int qi = qw + (lane & 15);         // the lane's query
   const int64_t base = (int64_t)b * S;
-  float qv[DH], o[DH];
+  const uint16_t* kh = k + base * D + h * DH;
+  const uint16_t* vh = v + base * D + h * DH;
+
+  bf16x8_t qf[DH / 32];                    // B operand: Q[qi][32c + 8·g4 .. +8]
 #pragma unroll
-  for (int d = 0; d < DH; ++d) {
-    qv[d] = live ? bf16_val(q[(base + i) * D + h * DH + d]) : 0.0f;
-    o[d] = 0.0f;
+  for (int c = 0; c < DH / 32; ++c) {
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (qi < S) w = *reinterpret_cast<const u32x4_t*>(q + (base + qi) * D + h * DH + 32 * c + 8 * g4);
+    qf[c] = __builtin_bit_cast(bf16x8_t, w);
   }
+  f32x4_t o[DH / 16];                      // Oᵀ[16d + 4·g4 + r][qi]
+#pragma unroll
+  for (int d = 0; d < DH / 16; ++d) o[d] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   float m = -INFINITY, l = 0.0f;
-  const int kend = min(S, q0 + NT);
+
+  const int kend = min(S, qb + 64);
   for (int t0 = 0; t0 < kend; t0 += KT) {
     __syncthreads();
-    for (int e = threadIdx.x; e < KT * DH; e += NT) {
-      const int j = e / DH, d = e % DH, key = t0 + j;
-      const bool ok = key < S;
-      ks[j][d] = ok ? bf16_val(k[(base + key) * D + h * DH + d]) : 0.0f;
-      vs[j][d] = ok ? bf16_val(v[(base + key) * D + h * DH + d]) : 0.0f;
+    for (int e = threadIdx.x; e < KT * DH / 8; e += NT) {
+      // K: consecutive threads along a key row
+      const int key = e / (DH / 8), c = e % (DH / 8);
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (t0 + key < S) w = *reinterpret_cast<const u32x4_t*>(kh + (int64_t)(t0 + key) * D + 8 * c);
+      *reinterpret_cast<u32x4_t*>(ks + key * KS + 8 * c) = w;
+      // Vᵀ: consecutive threads along keys, so the transposed writes are adjacent
+      const int vk = e % KT, vc = e / KT;
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (t0 + vk < S) x = *reinterpret_cast<const u32x4_t*>(vh + (int64_t)(t0 + vk) * D + 8 * vc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        vt[(8 * vc + i) * VS + vk] = (uint16_t)(x[i >> 1] >> (16 * (i & 1)));
     }
     __syncthreads();
-    if (live && t0 <= i) {
-      float s[KT];
-      float tmax = -INFINITY;
+    if (t0 > qw + 15) continue;            // every key after every query of the wave
+
+    f32x4_t sc[4];
 #pragma unroll
-      for (int j = 0; j < KT; ++j) {
-        float dot = 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      sc[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int d = 0; d < DH; ++d) dot = fmaf(qv[d], ks[j][d], dot);
-        s[j] = (t0 + j <= i) ? dot * scale : -INFINITY;
-        tmax = fmaxf(tmax, s[j]);
+      for (int c = 0; c < DH / 32; ++c) {
+        const bf16x8_t ka =
+            *reinterpret_cast<const bf16x8_t*>(ks + (16 * j + (lane & 15)) * KS + 32 * c + 8 * g4);
+        sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[c], sc[j], 0, 0, 0);
       }
-      const float mn = fmaxf(m, tmax);
-      const float corr = expf(m - mn);
-      l *= corr;
+    }
+    float s[16];
+    float tmax = -INFINITY;
 #pragma unroll
-      for (int d = 0; d < DH; ++d) o[d] *= corr;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < KT; ++j) {
-        const float p = (t0 + j <= i) ? expf(s[j] - mn) : 0.0f;
+      for (int r = 0; r < 4; ++r) {
+        const int key = t0 + 16 * j + 4 * g4 + r;
+        const float x = (key <= qi && key < S) ? sc[j][r] * scale_log2e : -INFINITY;
+        s[4 * j + r] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mn = fmaxf(m, tmax);       // finite: key 0 is in every query's first tile
+    const float corr = exp2f(m - mn);
+    m = mn;
+    l *= corr;
+#pragma unroll
+    for (int d = 0; d < DH / 16; ++d) o[d] *= corr;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {       // keys 32·h2 .. +31 of the tile
+      bf16x8_t ph, pm, pl;
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) {     // e2 < 4: block 2·h2, else block 2·h2 + 1
+        const float p = exp2f(s[8 * h2 + e2] - mn);
         l += p;
-#pragma unroll
-        for (int d = 0; d < DH; ++d) o[d] = fmaf(p, vs[j][d], o[d]);
+        const __bf16 hi = (__bf16)p;
+        const float r1 = p - (float)hi;    // exact
+        const __bf16 mid = (__bf16)r1;
+        ph[e2] = hi;
+        pm[e2] = mid;
+        pl[e2] = (__bf16)(r1 - (float)mid);
       }
-      m = mn;
+#pragma unroll
+      for (int d = 0; d < DH / 16; ++d) {
+        const uint16_t* vr = vt + (16 * d + (lane & 15)) * VS + 32 * h2 + 4 * g4;
+        const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vr);
+        const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vr + 16);
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, u32x4_t{v0[0], v0[1], v1[0], v1[1]});
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pm, o[d], 0, 0, 0);
+        o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, o[d], 0, 0, 0);
+      }
     }
   }
-  if (live) {
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (qi < S) {
     const float inv = 1.0f / l;
+    uint16_t* orow = out + (base + qi) * D + h * DH + 4 * g4;
 #pragma unroll
-    for (int d = 0; d < DH; ++d)
-      out[(base + i) * D + h * DH + d] = (uint16_t)bf16_bits(o[d] * inv);
+    for (int d = 0; d < DH / 16; ++d) {
+      const uint32_t lo = bf16_bits(o[d][0] * inv) | (bf16_bits(o[d][1] * inv) << 16);
+      const uint32_t hi = bf16_bits(o[d][2] * inv) | (bf16_bits(o[d][3] * inv) << 16);
+      *reinterpret_cast<u32x2_t*>(orow + 16 * d) = u32x2_t{lo, hi};
+    }
   }
 }
 
@@ -209,14 +277,14 @@ ar_status linear(const LinearWs& w, const uint16_t* x, const uint16_t* W, uint16
 
 ar_status attention(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                     uint16_t* out, hipStream_t st) {
-  const dim3 grid((unsigned)(d.B * d.H), (unsigned)((d.S + NT - 1) / NT));
-  const float scale = (float)(1.0 / sqrt((double)d.Dh));
+  const dim3 grid((unsigned)(d.B * d.H), (unsigned)((d.S + 63) / 64));
+  const float sl = (float)(1.4426950408889634 / sqrt((double)d.Dh));   // log2(e)/sqrt(Dh)
   if (d.Dh == 64)
     hipLaunchKernelGGL(k_attention<64>, grid, dim3(NT), 0, st, q, k, v, out, (int)d.D, (int)d.S,
-                       (int)d.H, scale);
+                       (int)d.H, sl);
   else if (d.Dh == 128)
     hipLaunchKernelGGL(k_attention<128>, grid, dim3(NT), 0, st, q, k, v, out, (int)d.D, (int)d.S,
-                       (int)d.H, scale);
+                       (int)d.H, sl);
   else
     return AR_ERR_UNSUPPORTED;
   return last_status();
@@ -396,6 +464,16 @@ ar_status ar_block_forward(const ar_block_dims* bd, const ar_block_weights* wts,
   if (hipMemcpyAsync(out, w.fp.out, (size_t)(d.M * d.D) * 2, hipMemcpyDeviceToDevice, st))
     return AR_ERR_HIP;
   return AR_OK;
+}
+
+ar_status ar_attention(const ar_block_dims* bd, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, uint16_t* out, void* stream) {
+  Dims d;
+  AR_TRY(check_dims(bd, &d));
+  if (!q || !k || !v || !out) return AR_ERR_INVALID_ARG;
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if (!a16(q) || !a16(k) || !a16(v) || !a16(out)) return AR_ERR_INVALID_ARG;
+  return attention(d, q, k, v, out, static_cast<hipStream_t>(stream));
 }
 
 ar_status ar_tune_block(const ar_config* cfg, const ar_block_dims* bd,

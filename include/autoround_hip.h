@@ -258,6 +258,14 @@ ar_status ar_block_forward(const ar_block_dims* dims, const ar_block_weights* w,
                            const uint16_t* h, uint16_t* out, void* ws, size_t ws_bytes,
                            void* stream);
 
+/* The block's attention step alone: out = causal softmax(q·kᵀ/sqrt(Dh))·v per
+   sequence (dims->seqlen consecutive rows) and head (dims->heads column groups
+   of Dh = hidden/heads, 64 or 128), with q and k already rotated. q, k, v, out
+   [nsamples·seqlen, hidden] bf16 row-major, 16-byte aligned; float32
+   accumulation and softmax, bf16 output. No workspace. */
+ar_status ar_attention(const ar_block_dims* dims, const uint16_t* q, const uint16_t* k,
+                       const uint16_t* v, uint16_t* out, void* stream);
+
 /* Tune the block's seven Linears in order q, k, v, o, gate, up, down, each with
    ar_tune_linear on target Y = its full-precision output (the block with the
    original weights on h) and input X = its input in the quantized pipeline

@@ -82,3 +82,60 @@ def test_block_forward_llama7b_dims():
     err = rel_norm(to_np(out), ref)
     log(f"  7B block forward rel err {err:.2e}")
     assert err <= 1e-2
+
+
+def _qkv(M, D, seed, qk_scale=1.0):
+    rng = np.random.default_rng(seed)
+    q, k, v = (synth.f32_to_bf16_bits((rng.standard_normal((M, D)) * s).astype(np.float32))
+               for s in (qk_scale, qk_scale, 1.0))
+    return q, k, v
+
+
+@pytest.mark.parametrize("D,H,S,nseq,qk_scale", [
+    (256, 4, 64, 4, 1.0),       # the toy block's heads (Dh 64)
+    (256, 4, 100, 3, 1.0),      # a sequence length that is not a multiple of the 64-key tile
+    (512, 4, 200, 2, 4.0),      # Dh 128, peaked softmax (scores with standard deviation 16)
+])
+def test_attention_against_oracle(D, H, S, nseq, qk_scale):
+    """The attention step (ar_attention) against the oracle's float64 causal
+    softmax on the same bf16 q, k, v. The GPU works in float32 (scores,
+    softmax weights split into three bf16 parts, accumulation), so before the
+    final bf16 rounding each output is within a few float32 roundings of
+    sum(p·|v|) <= max|v| of the oracle's; after it, the two differ by at most
+    one bf16 rounding step (2^-7 relative at worst) where a rounding boundary
+    falls between them, which few elements see."""
+    M = S * nseq
+    qb, kb, vb = _qkv(M, D, seed=S + D, qk_scale=qk_scale)
+    dims = ar.block_dims(D, H, 64, S, nseq)
+    out = ar.attention(bf16_dev(qb), bf16_dev(kb), bf16_dev(vb), dims)
+    torch.cuda.synchronize()
+    ref = B.attention(*(synth.bf16_bits_to_f32(x) for x in (qb, kb, vb)), S, H)
+    got = to_np(out)
+    err = rel_norm(got, ref)
+    same = np.mean(got == ref)
+    log(f"  attention D={D} H={H} S={S} x{nseq}: rel err {err:.2e}, identical {same:.5f}, "
+        f"max |diff| {np.abs(got - ref).max():.2e}")
+    assert err <= 1e-3
+    assert same >= 0.99
+    vmax = np.abs(synth.bf16_bits_to_f32(vb)).max()
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-5 * vmax)
+
+
+def test_attention_llama7b_heads():
+    """Llama-7B attention shapes (32 heads of 128, two 2048-token sequences),
+    checked on sampled heads: each head's columns of q, k, v form an attention
+    problem of their own for the oracle."""
+    D, H, S, nseq = 4096, 32, 2048, 2
+    qb, kb, vb = _qkv(S * nseq, D, seed=7)
+    dims = ar.block_dims(D, H, 11008, S, nseq)
+    out = ar.attention(bf16_dev(qb), bf16_dev(kb), bf16_dev(vb), dims)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    for h in (0, 13, 31):
+        cols = slice(128 * h, 128 * (h + 1))
+        ref = B.attention(*(synth.bf16_bits_to_f32(x[:, cols]) for x in (qb, kb, vb)), S, 1)
+        err = rel_norm(got[:, cols], ref)
+        same = np.mean(got[:, cols] == ref)
+        log(f"  head {h}: rel err {err:.2e}, identical {same:.5f}")
+        assert err <= 1e-3
+        assert same >= 0.99
