@@ -423,17 +423,25 @@ def dequant_gemm(X, qweight, qzeros, scale, bits: int, group_size: int, N: int, 
     return Y
 
 
-def pack(codes, zp, bits: int, stream=None):
-    """qweight [K*bits/32, N] int32 and qzeros [G, N*bits/32] int32 (or None)."""
+def pack(codes, zp, bits: int, stream=None, out=None):
+    """qweight [K*bits/32, N] int32 and qzeros [G, N*bits/32] int32 (or None).
+    ``out`` = (qweight, qzeros) writes into given tensors instead."""
     torch = _torch()
     _dev(codes, zp)
     N, K = codes.shape
-    qw = torch.empty((K * bits // 32, N), dtype=torch.int32, device=codes.device)
-    qz = None
-    G = 0
-    if zp is not None:
-        G = zp.shape[1]
-        qz = torch.empty((G, N * bits // 32), dtype=torch.int32, device=codes.device)
+    G = 0 if zp is None else zp.shape[1]
+    if out is not None:
+        qw, qz = out
+        _dev(qw, qz)
+        if tuple(qw.shape) != (K * bits // 32, N) or qw.dtype != torch.int32 or \
+                (zp is not None and (qz is None or tuple(qz.shape) != (G, N * bits // 32)
+                                     or qz.dtype != torch.int32)):
+            raise ValueError("out tensors do not match the packed shapes")
+    else:
+        qw = torch.empty((K * bits // 32, N), dtype=torch.int32, device=codes.device)
+        qz = None
+        if zp is not None:
+            qz = torch.empty((G, N * bits // 32), dtype=torch.int32, device=codes.device)
     _check(lib.ar_pack(bits, _ptr(codes), _ptr(zp), N, K, G, _ptr(qw), _ptr(qz),
                        _stream(stream)), "ar_pack")
     return qw, qz

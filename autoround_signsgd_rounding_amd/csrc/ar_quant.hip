@@ -323,18 +323,69 @@ __device__ __forceinline__ uint32_t get_code(const uint32_t* in, int c) {
 // codes [N, K] -> qweight [K*BITS/32, N]. A workgroup stages a 64 x 256 code
 // tile in LDS (coalesced row reads), then each thread packs one block of one
 // row and the stores of consecutive threads hit consecutive columns.
+// The WB words of one block of CB codes, one code per byte at b (16-byte
+// aligned LDS), each masked to BITS bits, LSB first. 4- and 2-bit codes are
+// merged within each 32-bit word by shifts, then gathered with v_perm.
 template <int BITS>
+__device__ __forceinline__ void pack_block(const uint8_t* b, uint32_t (&out)[PackShape<BITS>::WB]) {
+  if constexpr (BITS == 8) {
+    out[0] = *reinterpret_cast<const uint32_t*>(b);
+  } else if constexpr (BITS == 4) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(b);
+    const uint32_t x = v[0] & 0x0F0F0F0Fu, y = v[1] & 0x0F0F0F0Fu;
+    // bytes 0 and 2 of x | x >> 4 hold codes (0,1) and (2,3)
+    out[0] = __builtin_amdgcn_perm(y | (y >> 4), x | (x >> 4), 0x06040200u);
+  } else if constexpr (BITS == 2) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(b);
+    uint32_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = v[i] & 0x03030303u;
+      const uint32_t t = (x | (x >> 6)) & 0x000F000Fu;   // codes (0,1) at bit 0, (2,3) at 16
+      u[i] = t | (t >> 12);                               // four codes in byte 0
+    }
+    out[0] = __builtin_amdgcn_perm(u[1], u[0], 0x0C0C0400u) |
+             (__builtin_amdgcn_perm(u[3], u[2], 0x0C0C0400u) << 16);
+  } else {
+    const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(b);
+    const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(b + 16);
+    uint32_t o[PackShape<BITS>::WB + 1] = {};
+#pragma unroll
+    for (int c = 0; c < PackShape<BITS>::CB; ++c) {
+      const uint32_t w = c < 16 ? v0[(c >> 2) & 3] : v1[(c >> 2) & 3];
+      put_code<BITS>(o, c, (w >> (8 * (c & 3))) & PackShape<BITS>::MASK);
+    }
+#pragma unroll
+    for (int w = 0; w < PackShape<BITS>::WB; ++w) out[w] = o[w];
+  }
+}
+
+// codes [N, K] -> qweight [K*BITS/32, N] through an LDS tile of 64 rows x 256
+// codes: coalesced 16-byte loads along K (4-byte loads when K % 16 != 0), and
+// word stores coalesced along N.
+constexpr int PK_ROW = 256 + 16;   // LDS bytes per tile row
+template <int BITS, bool V16>
 __global__ __launch_bounds__(NT) void k_pack_w(const uint8_t* __restrict__ codes,
                                                uint32_t* __restrict__ qw, int64_t N, int64_t K) {
   using S = PackShape<BITS>;
-  __shared__ uint32_t tile[64][65];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64 * PK_ROW];
   const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 256;
-  for (int i = threadIdx.x; i < 64 * 64; i += NT) {
-    const int r = i >> 6, c = i & 63;
-    const int64_t n = n0 + r, k = k0 + 4 * c;
-    uint32_t v = 0;
-    if (n < N && k < K) v = *reinterpret_cast<const uint32_t*>(codes + n * K + k);
-    tile[r][c] = v;
+  if constexpr (V16) {
+    for (int i = threadIdx.x; i < 64 * 16; i += NT) {
+      const int r = i >> 4, c = i & 15;
+      const int64_t n = n0 + r, k = k0 + 16 * c;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (n < N && k < K) v = *reinterpret_cast<const u32x4_t*>(codes + n * K + k);
+      *reinterpret_cast<u32x4_t*>(tile + r * PK_ROW + 16 * c) = v;
+    }
+  } else {
+    for (int i = threadIdx.x; i < 64 * 64; i += NT) {
+      const int r = i >> 6, c = i & 63;
+      const int64_t n = n0 + r, k = k0 + 4 * c;
+      uint32_t v = 0;
+      if (n < N && k < K) v = *reinterpret_cast<const uint32_t*>(codes + n * K + k);
+      *reinterpret_cast<uint32_t*>(tile + r * PK_ROW + 4 * c) = v;
+    }
   }
   __syncthreads();
   constexpr int NB = 256 / S::CB;
@@ -343,30 +394,69 @@ __global__ __launch_bounds__(NT) void k_pack_w(const uint8_t* __restrict__ codes
     const int r = it & 63, blk = it >> 6;
     const int64_t n = n0 + r, kb = k0 + (int64_t)blk * S::CB;
     if (n >= N || kb >= K) continue;
-    uint32_t out[S::WB + 1] = {};
-    for (int c = 0; c < S::CB; ++c) {
-      const int byte = blk * S::CB + c;
-      put_code<BITS>(out, c, (tile[r][byte >> 2] >> (8 * (byte & 3))) & S::MASK);
-    }
+    uint32_t out[S::WB];
+    pack_block<BITS>(tile + r * PK_ROW + blk * S::CB, out);
 #pragma unroll
     for (int w = 0; w < S::WB; ++w) qw[(wrow0 + (int64_t)blk * S::WB + w) * N + n] = out[w];
   }
 }
 
-// zp [N, G] -> qzeros [G, N*BITS/32]: same bit layout along N.
+// zp [N, G] -> qzeros [G, N*BITS/32]: the same bit layout along N. A workgroup
+// takes 256 columns and PZ_G groups into an LDS tile transposed to
+// [group][column], then stores each group's words contiguously. When one chunk
+// holds every group, the workgroup's zero-points are one contiguous run of
+// rows·G bytes (16-byte aligned with zp: 256·G is a multiple of 16), read in
+// 16-byte pieces whatever G is.
+constexpr int PZ_G = 128;
 template <int BITS>
 __global__ __launch_bounds__(NT) void k_pack_z(const uint8_t* __restrict__ zp,
                                                uint32_t* __restrict__ qz, int64_t N, int64_t G) {
   using S = PackShape<BITS>;
-  const int64_t nblk = N / S::CB;
-  const int64_t idx = (int64_t)blockIdx.x * NT + threadIdx.x;
-  if (idx >= G * nblk) return;
-  const int64_t j = idx / nblk, blk = idx - j * nblk;
-  uint32_t out[S::WB + 1] = {};
-  for (int c = 0; c < S::CB; ++c) put_code<BITS>(out, c, zp[(blk * S::CB + c) * G + j] & S::MASK);
+  __shared__ __attribute__((aligned(16))) uint8_t tile[PZ_G * PK_ROW];
+  const int64_t n0 = (int64_t)blockIdx.x * 256, j0 = (int64_t)blockIdx.y * PZ_G;
+  const int gc = (int)(G - j0 < PZ_G ? G - j0 : PZ_G);
+  const int rows = (int)(N - n0 < 256 ? N - n0 : 256);
   const int64_t words = N * BITS / 32;
+  constexpr int NB = 256 / S::CB;
+  if (gc == G && (reinterpret_cast<uintptr_t>(zp) & 15) == 0) {
+    const uint8_t* run = zp + n0 * G;
+    const int len = rows * (int)G, full = len / 16;
+    for (int i = threadIdx.x; i < full; i += NT) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(run + 16 * i);
+      int r = 16 * i / (int)G, c = 16 * i - r * (int)G;
 #pragma unroll
-  for (int w = 0; w < S::WB; ++w) qz[j * words + blk * S::WB + w] = out[w];
+      for (int e = 0; e < 16; ++e) {
+        tile[c * PK_ROW + r] = (uint8_t)(v[e >> 2] >> (8 * (e & 3)));
+        if (++c == (int)G) {
+          c = 0;
+          ++r;
+        }
+      }
+    }
+    for (int o = 16 * full + threadIdx.x; o < len; o += NT) {
+      const int r = o / (int)G, c = o - r * (int)G;
+      tile[c * PK_ROW + r] = run[o];
+    }
+  } else {
+    for (int i = threadIdx.x; i < rows * gc; i += NT) {
+      const int r = i / gc, c = i - r * gc;
+      tile[c * PK_ROW + r] = zp[(n0 + r) * G + j0 + c];
+    }
+  }
+  for (int i = threadIdx.x; i < (256 - rows) * gc; i += NT) {   // past N: zero
+    const int r = rows + i / gc, c = i % gc;
+    tile[c * PK_ROW + r] = 0;
+  }
+  __syncthreads();
+  for (int it = threadIdx.x; it < gc * NB; it += NT) {
+    const int jj = it / NB, blk = it - jj * NB;
+    if (blk * S::CB >= rows) continue;
+    uint32_t out[S::WB];
+    pack_block<BITS>(tile + jj * PK_ROW + blk * S::CB, out);
+#pragma unroll
+    for (int w = 0; w < S::WB; ++w)
+      qz[(j0 + jj) * words + (n0 / S::CB + blk) * S::WB + w] = out[w];
+  }
 }
 
 template <int BITS>
@@ -538,10 +628,14 @@ ar_status ar_launch_pack(int bits, const uint8_t* codes, const uint8_t* zp, int6
   switch (bits) {
 #define AR_PACK_CASE(B)                                                                       \
   case B:                                                                                     \
-    hipLaunchKernelGGL(k_pack_w<B>, gw, dim3(NT), 0, st, codes, qw, N, K);                    \
+    if (K % 16 == 0)                                                                          \
+      hipLaunchKernelGGL((k_pack_w<B, true>), gw, dim3(NT), 0, st, codes, qw, N, K);          \
+    else                                                                                      \
+      hipLaunchKernelGGL((k_pack_w<B, false>), gw, dim3(NT), 0, st, codes, qw, N, K);         \
     if (zp)                                                                                   \
-      hipLaunchKernelGGL(k_pack_z<B>, dim3(blocks_for(G * (N / PackShape<B>::CB))), dim3(NT), \
-                         0, st, zp, qz, N, G);                                                \
+      hipLaunchKernelGGL(k_pack_z<B>, dim3((unsigned)((N + 255) / 256),                        \
+                                           (unsigned)((G + PZ_G - 1) / PZ_G)),                 \
+                         dim3(NT), 0, st, zp, qz, N, G);                                      \
     break;
     AR_PACK_CASE(2) AR_PACK_CASE(3) AR_PACK_CASE(4) AR_PACK_CASE(8)
 #undef AR_PACK_CASE

@@ -125,6 +125,11 @@ def test_empty_is_noop():
 
 
 PACK_CASES = [(b, N, K) for b in (2, 3, 4, 8) for (N, K) in ((32, 32), (96, 288), (224, 544))]
+# K % 16 != 0 (4-byte loads of the codes); 80, 86, 128 and 256 groups (the
+# zero-points of a column block read as one run whatever G is, or in chunks of
+# 128 groups); a column count that leaves a partial 256-column block
+PACK_CASES += [(8, 64, 36), (4, 96, 40), (4, 40, 520), (4, 64, 4096), (3, 96, 2560), (4, 32, 8192),
+               (2, 320, 2752)]
 
 
 @pytest.mark.parametrize("bits,N,K", PACK_CASES)
