@@ -187,3 +187,55 @@ def test_pack_validation():
     assert pk(4, NULL, NULL, 8, 128, 1, P, NULL, NULL) == INV
     assert pk(4, P, NULL, 0, 128, 1, P, NULL, NULL) == OK
     assert ar.lib.ar_unpack(16, P, NULL, 8, 128, 1, P, NULL, NULL) == UNSUP
+
+
+def dq_ws(bits=4, g=128, M=1, N=4096, K=4096):
+    n = ctypes.c_size_t(12345)
+    st = ar.lib.ar_dequant_gemm_workspace_size(bits, g, M, N, K, ctypes.byref(n))
+    return st, n.value
+
+
+def test_dequant_workspace_validation():
+    assert dq_ws(bits=5)[0] == UNSUP
+    assert dq_ws(g=0)[0] == INV
+    assert dq_ws(g=12)[0] == UNSUP            # groups must be a multiple of 8
+    assert dq_ws(g=64, K=96)[0] == SHAPE      # K % group
+    assert dq_ws(K=12)[0] == SHAPE            # K % 8
+    assert dq_ws(M=0) == (OK, 0)
+    assert ar.lib.ar_dequant_gemm_workspace_size(4, 128, 1, 64, 128, None) == INV
+    for M in (1, 16, 17, 300):
+        st, n = dq_ws(M=M)
+        assert st == OK and n > 0 and n % 256 == 0
+    # small M: one float32 partial per (slice, row, column), a whole number of slices
+    st1, n1 = dq_ws(M=1, N=4096)
+    assert n1 % (4096 * 4) == 0 and n1 // (4096 * 4) >= 1
+    st2, n2 = dq_ws(M=2, N=4096)
+    assert n2 % (2 * 4096 * 4) == 0
+
+
+def dq(X=P, M=1, K=4096, qw=P, qz=P, sc=P, N=4096, Y=P, ydt=0, ws=P, wsb=1 << 30, g=128, bits=4):
+    return ar.lib.ar_dequant_gemm(bits, g, X, M, K, qw, qz, sc, N, Y, ydt, ws, wsb, NULL)
+
+
+def test_dequant_validation():
+    assert dq(X=NULL) == INV
+    assert dq(Y=NULL) == INV
+    assert dq(qw=NULL) == INV
+    assert dq(X=P_MIS) == INV
+    assert dq(ydt=7) == UNSUP
+    assert dq(bits=6) == UNSUP
+    assert dq(g=-2) == INV
+    assert dq(wsb=16) == WS
+    assert dq(N=30, qz=P, bits=3) == SHAPE     # zero-point words need N*bits % 32 == 0
+    assert dq(M=0) == OK and dq(N=0) == OK     # no-ops
+
+
+def test_attention_validation():
+    d = ar.block_dims(256, 4, 512, 64, 2)
+    A = ar.lib.ar_attention
+    assert A(None, P, P, P, P, NULL) == INV
+    assert A(ctypes.byref(d), NULL, P, P, P, NULL) == INV
+    assert A(ctypes.byref(d), P, P, P_MIS, P, NULL) == INV
+    bad = ar.block_dims(384, 4, 512, 64, 2)    # head dim 96
+    assert A(ctypes.byref(bad), P, P, P, P, NULL) == UNSUP
+    assert A(ctypes.byref(ar.block_dims(256, 3, 512, 64, 2)), P, P, P, P, NULL) == SHAPE
