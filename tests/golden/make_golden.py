@@ -7,6 +7,7 @@ factors, plus the whole loss trajectory and the best step.
 
     python tests/golden/make_golden.py llama7b_q_proj          # ~15 min on 8 cores
     python tests/golden/make_golden.py llama7b_q_proj --gram   # the oracle's Gram mode
+    python tests/golden/make_golden.py --block                 # Llama-7B-shaped block, see below
 """
 import os
 import sys
@@ -64,6 +65,47 @@ def main(name, gram=False):
           f"codes changed vs RTN {(res.codes != rtn_codes).mean():.4f}", flush=True)
 
 
+# Block-wise tuning at the Llama-7B block shape (D 4096, 32 heads, F 11008), kept
+# small enough for the oracle: 2 sequences of 2048 tokens, minibatches of one
+# sequence, 2 iterations per Linear, W4 g128 asym, quantized inputs.
+BLOCK_NSAMPLES, BLOCK_ITERS = 2, 2
+N_BLOCK_ROWS = 32
+
+
+def main_block():
+    from oracle import block_ref as B
+    dims = synth.BLOCKS["llama7b_block"]
+    t0 = time.time()
+    c = synth.make_block_case(dims, nsamples=BLOCK_NSAMPLES)
+    od = synth.BlockDims(dims.name, dims.D, dims.H, dims.F, dims.seqlen, BLOCK_NSAMPLES,
+                         dims.rms_eps, dims.rope_theta)
+    W = {n: synth.bf16_bits_to_f32(c.W_bits[n]) for n in B.LINEARS}
+    norms = tuple(synth.bf16_bits_to_f32(x) for x in c.norm_bits)
+    h = synth.bf16_bits_to_f32(c.H_bits)
+    cfg = O.Config(bits=4, group_size=128, nsamples=BLOCK_NSAMPLES, seqlen=dims.seqlen,
+                   batch_samples=1, iters=BLOCK_ITERS)
+    print(f"inputs ready {time.time() - t0:.1f}s", flush=True)
+    r = B.tune_block(h, W, norms, od, cfg, quanted_input=True)
+    rng = np.random.default_rng(ROW_SEED)
+    out = {"err": np.float64(r.err)}
+    for n in B.LINEARS:
+        res = r.results[n]
+        rows = np.sort(rng.choice(res.codes.shape[0], size=N_BLOCK_ROWS, replace=False))
+        out[f"{n}_losses"] = np.array(res.losses, np.float64)
+        out[f"{n}_rows"] = rows
+        out[f"{n}_codes"] = res.codes[rows]
+    trows = np.sort(rng.choice(r.out_q.shape[0], size=64, replace=False))
+    out["token_rows"] = trows
+    out["out_fp"] = r.out_fp[trows]
+    out["out_q"] = r.out_q[trows]
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tune_block_llama7b.npz")
+    np.savez_compressed(path, **out)
+    print(f"wrote {path}; block output mse {r.err:.6e}; t={time.time() - t0:.0f}s", flush=True)
+
+
 if __name__ == "__main__":
     args = [a for a in sys.argv[1:] if not a.startswith("--")]
-    main(args[0] if args else "llama7b_q_proj", gram="--gram" in sys.argv)
+    if "--block" in sys.argv:
+        main_block()
+    else:
+        main(args[0] if args else "llama7b_q_proj", gram="--gram" in sys.argv)

@@ -7,6 +7,8 @@ so a rounding can land on the other side of a bf16 boundary. Comparisons are
 therefore norm-wise: the block output within 1e-2, per-Linear losses within
 1e-3 for q/k/v (identical inputs) and within 2e-2 further down, codes at least
 99% identical."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -18,6 +20,7 @@ from gpu_common import bf16_dev, dev, log, rel_norm, to_np
 
 pytestmark = pytest.mark.gpu
 ar = pytest.importorskip("autoround_signsgd_rounding_amd")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def _setup(name, nsamples=None):
@@ -139,3 +142,38 @@ def test_attention_llama7b_heads():
         log(f"  head {h}: rel err {err:.2e}, identical {same:.5f}")
         assert err <= 1e-3
         assert same >= 0.99
+
+
+def test_tune_block_llama7b_against_oracle_golden():
+    """Block-wise tuning at the Llama-7B block shape (D 4096, 32 heads, F 11008;
+    2 sequences of 2048 tokens, one per minibatch, 2 iterations per Linear, W4
+    g128 asym, quantized inputs) against the oracle's own run stored by
+    tests/golden/make_golden.py --block: every Linear's loss trajectory, the
+    codes of 32 sampled rows per Linear, and 64 sampled rows of both block
+    outputs, with the toy block's tolerances."""
+    path = os.path.join(GOLDEN, "tune_block_llama7b.npz")
+    if not os.path.exists(path):
+        pytest.skip("golden file not generated")
+    gold = np.load(path)
+    od, bd, Wd, nd, hd, W, norms, h = _setup("llama7b_block", nsamples=2)
+    cfg = ar.Config(bits=4, group_size=128, nsamples=2, seqlen=od.seqlen, batch_samples=1,
+                    iters=2)
+    res, out_fp, out_q = ar.tune_block(hd, Wd, nd, bd, cfg, quanted_input=True)
+    torch.cuda.synchronize()
+    for i, n in enumerate(B.LINEARS):
+        codes, _, _, _, losses = res[n]
+        L = to_np(losses).astype(np.float64)
+        Lo = gold[f"{n}_losses"]
+        rows = torch.from_numpy(gold[f"{n}_rows"]).to(dev())
+        agree = np.mean(to_np(codes[rows]) == gold[f"{n}_codes"])
+        tol = 1e-3 if i < 3 else 2e-2
+        log(f"  {n}: losses {L} vs {Lo}; sampled codes agree {agree:.5f}")
+        assert np.all(np.abs(L - Lo) <= tol * Lo)
+        assert agree >= 0.99
+    trows = torch.from_numpy(gold["token_rows"]).to(dev())
+    efp = rel_norm(to_np(out_fp[trows]), gold["out_fp"])
+    eq = rel_norm(to_np(out_q[trows]), gold["out_q"])
+    e_gpu = float(np.mean((to_np(out_q).astype(np.float64) - to_np(out_fp)) ** 2))
+    log(f"  outputs rel err fp {efp:.2e} q {eq:.2e}; mse {e_gpu:.5e} vs {float(gold['err']):.5e}")
+    assert efp <= 1e-2 and eq <= 1e-2
+    assert abs(e_gpu - float(gold["err"])) <= 0.05 * float(gold["err"])
