@@ -57,7 +57,7 @@ def _measured_traffic(workload):
     return int(float(kv["traffic_bytes"]))
 
 
-def _cpu_baseline(case, Yd, w, steps=2):
+def _cpu_baseline(case, Yd, w, steps=8):
     """The CPU oracle as it stands, timed on `steps` SignSGD steps of the same
     workload (full 4096x4096 problem, Tb = 16384 tokens per step)."""
     import torch
