@@ -115,8 +115,9 @@ __global__ __launch_bounds__(NT) void k_dequant_blocked(DqArgs a, uint16_t* WB, 
 // no carries, as q + 128 − zp lies in [113, 143]), converted by
 // v_cvt_f32_ubyte, and fma(q + 128 − zp, s, −128·s) gives s·(q − zp) rounded
 // once, as the product of an exact integer and s is; v_cvt_pk_bf16_f32 rounds
-// two to bf16 (nearest even). 2 and 3 bits extract each code with a bit-field
-// extract instead; 8-bit codes are bytes, converted and then s·(q − zp).
+// two to bf16 (nearest even). 2-bit codes reach the same byte form through one
+// v_perm; 3-bit codes are extracted one by one with a bit-field extract; 8-bit
+// codes are bytes, converted and then s·(q − zp).
 constexpr int DQ_COLS = 256;        // columns per workgroup
 constexpr int DQ_GSTRIDE = DQ_COLS + 4;   // floats per staged group row (bank spread)
 constexpr int DQ_WG_COST = 96;      // fixed cost of a workgroup (staging), in units of k
@@ -127,7 +128,7 @@ constexpr int DQ_MAX_LK = 4096;     // longest slice (group-row table of Lk / 8 
 // Per-(group, column) zero-point term of the dequantization below.
 template <int BITS>
 __device__ __forceinline__ uint32_t zp_term(uint32_t zp) {
-  if constexpr (BITS == 4) return (128u - zp) * 0x01010101u;
+  if constexpr (BITS == 4 || BITS == 2) return (128u - zp) * 0x01010101u;
   else if constexpr (BITS == 8) return __float_as_uint((float)zp);
   else return 128u - zp;
 }
@@ -144,6 +145,17 @@ __device__ __forceinline__ bf16x8_t dq_chunk(uint32_t lo, uint32_t hi, uint32_t 
     for (int p = 0; p < 4; ++p) {
       b[2 * p] = (__bf16)fmaf((float)((L >> (8 * p)) & 0xFFu), s, nb);
       b[2 * p + 1] = (__bf16)fmaf((float)((H >> (8 * p)) & 0xFFu), s, nb);
+    }
+  } else if constexpr (BITS == 2) {
+    // x = c0..c7 (2 bits each); w = x >> 4 puts c2 at bit 0 of its low byte.
+    // perm gathers [x.b0, w.b0, x.b1, w.b1] = bytes starting at c0, c2, c4, c6.
+    const uint32_t x = (lo >> sh) & 0xFFFFu, w = x >> 4;
+    const uint32_t t = __builtin_amdgcn_perm(w, x, 0x05010400u);
+    const uint32_t E = (t & 0x03030303u) + z, O = ((t >> 2) & 0x03030303u) + z;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      b[2 * p] = (__bf16)fmaf((float)((E >> (8 * p)) & 0xFFu), s, nb);
+      b[2 * p + 1] = (__bf16)fmaf((float)((O >> (8 * p)) & 0xFFu), s, nb);
     }
   } else if constexpr (BITS == 8) {
     const float zf = __uint_as_float(z);
