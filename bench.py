@@ -205,6 +205,41 @@ def _decode_large(ar, torch, reps, N=29568, K=8192, bits=4, g=128):
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
 
 
+def _step_run(ar, torch, W, X, Y, cfg, w, warm=10, timed=30):
+    """ar_tune_step, one SignSGD iteration from caller-owned state per call on
+    the workload's minibatches in turn (each call stages its own minibatch):
+    HIP events around each call on the launch stream, median over `timed`
+    calls after `warm` untimed ones."""
+    dev = W.device
+    G = w.K // w.group_size
+    V = torch.zeros((w.N, w.K), dtype=torch.float32, device=dev)
+    a = torch.full((w.N, G), float(w.minmax_shrink), dtype=torch.float32, device=dev)
+    b = a.clone()
+    best = (torch.empty_like(V), torch.empty_like(a), torch.empty_like(b),
+            torch.full((1,), float("inf"), dtype=torch.float32, device=dev))
+    ydt = ar.AR_BF16 if Y.dtype == torch.bfloat16 else ar.AR_F32
+    ws = torch.empty(ar.step_workspace_size(cfg, w.N, w.K, w.Tb, ydt), dtype=torch.uint8,
+                     device=dev)
+    nb = w.nsamples // w.batch_samples
+    stream = torch.cuda.current_stream()
+    ms = []
+    for i in range(warm + timed):
+        j = i % nb
+        Xb, Yb = X[j * w.Tb:(j + 1) * w.Tb], Y[j * w.Tb:(j + 1) * w.Tb]
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        ar.tune_step(W, V, a, b, Xb, Yb, cfg, best=best, want_grads=False, workspace=ws)
+        e1.record(stream)
+        if i >= warm:
+            ms.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ms)
+    med = t[len(t) // 2]
+    return {"ms_median": round(med, 4), "iters_per_s": round(1e3 / med, 1),
+            "note": "per call, including the call's own transposition of its minibatch"}
+
+
 def _pack_time(ar, torch, out, bits, reps=20):
     """GPU time of one ar_pack of the tuned codes and zero-points: a HIP graph
     of `reps` calls into preallocated outputs, replayed between two events (the
@@ -456,6 +491,7 @@ def main():
             "input_gen_s": round(t_gen, 1),
         },
     }
+    line["detail"]["tune_step"] = _step_run(ar, torch, W, X, Y, cfg, w)
     line["detail"]["dequant_gemm"] = _dequant_run(ar, torch, X, recs[-1][1], w)
     if not args.no_block:
         line["detail"]["block"] = _block_run(ar, torch)
