@@ -199,10 +199,10 @@ __host__ __device__ constexpr int dq_batch() { return BITS == 4 ? 8 : BITS == 3 
 // LDS: X rows [M][Lp + 8] bf16, zero from the slice's end; scale, −128·scale
 // and zero-point term [groups][DQ_GSTRIDE]; the group-row offset of each
 // chunk [Lp / 8].
+// The launch bound caps registers at 128 VGPRs, for 4 waves per SIMD.
 template <int BITS, bool VEC>
-__global__ __launch_bounds__(NT, 4) void k_dq_mfma(   // at most 128 VGPRs: 4 waves per SIMD
-DqArgs a, const uint16_t* X, int M, float* part,
-                                                int Lk) {
+__global__ __launch_bounds__(NT, 4) void k_dq_mfma(DqArgs a, const uint16_t* X, int M, float* part,
+                                                   int Lk) {
   constexpr int B = dq_batch<BITS>();
   extern __shared__ __attribute__((aligned(16))) uint8_t dq_lds[];
   const int N = (int)a.N, K = (int)a.K, g = a.g;
@@ -221,7 +221,7 @@ DqArgs a, const uint16_t* X, int M, float* part,
   const int lcol = 64 * wave + 4 * (lane & 15);   // first of the lane's columns in the workgroup
   const int col = cb + lcol;
   const int q = lane >> 4;
-  const bool live = col < N;   // columns past N: words read as 0, s = 0, so B = 0
+  const bool live = col < N;   // columns past N have s = 0 (so B = 0) and are not stored
   // Step t reads packed word w0 + t·BITS of each column at the same bit offset
   // (32 codes are 32·BITS bits = BITS words).
   const uint32_t off0 = (uint32_t)(k0 + 8 * q) * BITS, sh = off0 & 31;
