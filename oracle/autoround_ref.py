@@ -33,7 +33,8 @@ accumulates the loss and the straight-through sums in float64.
 Every function here is pinned by a CPU test against something other than
 itself (hand-derived vectors, a nearest-grid search, brute force, torch
 autograd, the Gram identity, big-integer packing); see ``tests/test_oracle_pins.py``.
-Readings where the pages are silent or garbled are listed in the design doc.
+Where the pages are silent or garbled, the reading taken is stated in the
+function that takes it.
 """
 from __future__ import annotations
 
