@@ -177,3 +177,34 @@ def test_tune_block_llama7b_against_oracle_golden():
     log(f"  outputs rel err fp {efp:.2e} q {eq:.2e}; mse {e_gpu:.5e} vs {float(gold['err']):.5e}")
     assert efp <= 1e-2 and eq <= 1e-2
     assert abs(e_gpu - float(gold["err"])) <= 0.05 * float(gold["err"])
+
+
+def test_tune_block_chain_of_two_toy_blocks():
+    """Two blocks in sequence: block 2's full-precision input is block 1's
+    full-precision output and its quantized-pipeline input is block 1's
+    quantized output (h_q), so every Linear of block 2 is tuned on inputs that
+    carry block 1's quantization. Both blocks against the oracle's chain."""
+    od, bd, Wd, nd, hd, W, norms, h = _setup("toy_block")
+    cfg = ar.Config(bits=4, group_size=64, nsamples=od.nsamples, seqlen=od.seqlen,
+                    batch_samples=2, iters=5)
+    oc = O.Config(bits=4, group_size=64, nsamples=od.nsamples, seqlen=od.seqlen, batch_samples=2,
+                  iters=5)
+    res1, fp1, q1 = ar.tune_block(hd, Wd, nd, bd, cfg, quanted_input=True)
+    res2, fp2, q2 = ar.tune_block(fp1, Wd, nd, bd, cfg, quanted_input=True, h_q=q1)
+    torch.cuda.synchronize()
+    r1 = B.tune_block(h, W, norms, od, oc, quanted_input=True)
+    # the oracle's chain continues from its own block-1 outputs
+    r2 = B.tune_block(r1.out_fp, W, norms, od, oc, quanted_input=True, h_q=r1.out_q)
+    for res, r, tag in ((res1, r1, "block 1"), (res2, r2, "block 2")):
+        for i, n in enumerate(B.LINEARS):
+            codes, _, _, _, losses = res[n]
+            L = to_np(losses).astype(np.float64)
+            Lo = np.array(r.results[n].losses)
+            agree = np.mean(to_np(codes) == r.results[n].codes)
+            log(f"  {tag} {n}: best {L.min():.5e} vs {Lo.min():.5e}; codes agree {agree:.5f}")
+            assert np.all(np.abs(L - Lo) <= 2e-2 * Lo)
+            assert agree >= 0.99
+    assert rel_norm(to_np(q2), r2.out_q) <= 1e-2
+    e2 = float(np.mean((to_np(q2).astype(np.float64) - to_np(fp2)) ** 2))
+    log(f"  block 2 output mse {e2:.5e} vs oracle {r2.err:.5e}")
+    assert abs(e2 - r2.err) <= 0.05 * r2.err
