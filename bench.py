@@ -160,9 +160,10 @@ def _dequant_run(ar, torch, X, out, w, reps=20):
 
 
 def _decode_large(ar, torch, reps, N=29568, K=8192, bits=4, g=128):
-    """One-token product on a Qwen2.5-72B up_proj-sized W4 layer (random codes:
-    the speed does not depend on their values), graph-timed like the decode
-    sizes above; 121 MB of packed weight make the HBM roofline the honest bound."""
+    """One-token product on a Qwen2.5-72B up_proj-sized layer, W`bits` g`g`
+    (random codes: the speed does not depend on their values), graph-timed like
+    the decode sizes above; at 4 bits, 121 MB of packed weight make the HBM
+    roofline the honest bound."""
     dev = torch.device("cuda:0")
     gen = torch.Generator(device=dev)
     gen.manual_seed(0)
@@ -365,6 +366,10 @@ def main():
     ap.add_argument("--block-only", action="store_true",
                     help="only run the block-wise tuning measurement and print its record "
                          "(for a kernel-trace profile of that workload alone)")
+    ap.add_argument("--dequant-only", action="store_true",
+                    help="only run the one-token packed-format product on the 29568x8192 W4 "
+                         "layer at every bit width and print its record (for profiles of that "
+                         "kernel alone)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -389,6 +394,10 @@ def main():
 
     if args.block_only:
         print(json.dumps({"block": _block_run(ar, torch)}), flush=True)
+        return
+    if args.dequant_only:
+        print(json.dumps({"dequant_decode": [_decode_large(ar, torch, 20, bits=b)
+                                             for b in (4, 2, 3, 8)]}), flush=True)
         return
     w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
