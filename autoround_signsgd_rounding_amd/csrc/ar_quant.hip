@@ -261,38 +261,49 @@ __global__ __launch_bounds__(NT) void k_block_copy(const uint16_t* __restrict__ 
   }
 }
 
-// Row-major src [R, C] -> blocked dst with rows C and reduction R (a transpose),
-// zero padding; one thread per 8-element chunk of dst, consecutive threads on
-// consecutive src columns (coalesced reads).
+// Transposed staging: src [R rows, C cols] row-major -> blocked with C rows and
+// reduction R (dst row c holds src column c), zero padding. One workgroup per
+// destination block (256 dst rows x 32 reduction elements, contiguous in dst):
+// the 32 x 256 source tile is read with 16-byte loads along its rows into LDS,
+// and the block is written out linearly, 16 bytes per lane, each chunk
+// gathered from a tile column.
 template <typename T>
 __global__ __launch_bounds__(NT) void k_block_transpose(const T* __restrict__ src, T* __restrict__ dst,
                                                         int64_t R, int64_t C, int64_t nkb,
-                                                        int64_t src_batch, int64_t dst_batch) {
-  const int64_t rows = arblk::row_tiles(C) * arblk::ROWS;   // dst rows (padded)
-  const int64_t cpr = nkb * (arblk::KB / 8);
-  const int64_t total = rows * cpr;
-  const int64_t b = blockIdx.y;
+                                                        int64_t src_batch, int64_t dst_batch,
+                                                        int vec) {
+  constexpr int EPC = 16 / (int)sizeof(T);            // elements per 16-byte piece
+  constexpr int TS = arblk::ROWS + 16 / (int)sizeof(T); // tile row stride (elements)
+  __shared__ __attribute__((aligned(16))) T tile[arblk::KB * TS];
+  const int64_t rt = blockIdx.x, kb = blockIdx.y, b = blockIdx.z;
   src += b * src_batch;
-  dst += b * dst_batch;
-  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < total; i += (int64_t)gridDim.x * NT) {
-    const int64_t kc = i / rows, c = i - kc * rows;          // dst row c fastest
-    const int64_t r0 = kc * 8;
+  dst += b * dst_batch + ((rt * nkb + kb) << 13);   // the block: 8192 elements of T
+  const int64_t c0 = rt * arblk::ROWS, r0 = kb * arblk::KB;
+  constexpr int PPR = arblk::ROWS / EPC;               // pieces per tile row
+  for (int i = threadIdx.x; i < arblk::KB * PPR; i += NT) {
+    const int rk = i / PPR, pc = i - rk * PPR;
+    const int64_t r = r0 + rk, c = c0 + (int64_t)pc * EPC;
+    T v[EPC];
+    if (vec && r < R && c + EPC <= C) {
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src + r * C + c);
+      *reinterpret_cast<u32x4_t*>(v) = w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) v[e] = (r < R && c + e < C) ? src[r * C + c + e] : T(0);
+    }
+    *reinterpret_cast<u32x4_t*>(tile + rk * TS + pc * EPC) = *reinterpret_cast<const u32x4_t*>(v);
+  }
+  __syncthreads();
+  // chunk q of the block: dst row q / 4, stored chunk q % 4 = logical chunk ^ swizzle
+  for (int q = threadIdx.x; q < arblk::ROWS * 4; q += NT) {
+    const int rr = q >> 2, lc = (q & 3) ^ ((rr >> 2) & 3);
     T v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (c < C && r0 + e < R) ? src[(r0 + e) * C + c] : T(0);
-    T* d = dst + arblk::chunk_offset(c, r0, nkb);
-    if constexpr (sizeof(T) == 2) {
-      u32x4_t o;
+    for (int e = 0; e < 8; ++e) v[e] = tile[(8 * lc + e) * TS + rr];
+    T* d = dst + (int64_t)q * 8;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (uint32_t)v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
-      *reinterpret_cast<u32x4_t*>(d) = o;
-    } else {
-      u32x4_t o0, o1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { o0[e] = v[e]; o1[e] = v[4 + e]; }
-      reinterpret_cast<u32x4_t*>(d)[0] = o0;
-      reinterpret_cast<u32x4_t*>(d)[1] = o1;
-    }
+    for (int h = 0; h < 8 / EPC; ++h)
+      reinterpret_cast<u32x4_t*>(d)[h] = *reinterpret_cast<const u32x4_t*>(v + h * EPC);
   }
 }
 
@@ -593,17 +604,22 @@ ar_status ar_launch_block_copy(const uint16_t* src, uint16_t* dst, int64_t batch
 
 ar_status ar_launch_block_transpose(const void* src, void* dst, int64_t batch, int64_t R,
                                     int64_t C, int64_t nkb, int elem_bytes, hipStream_t st) {
-  const int64_t total = arblk::row_tiles(C) * arblk::ROWS * nkb * (arblk::KB / 8);
+  if (batch <= 0 || R <= 0 || C <= 0) return AR_OK;
+  if (nkb > 65535 || batch > 65535) return AR_ERR_SHAPE;   // grid y / z
   const int64_t dst_batch = arblk::row_tiles(C) * nkb * arblk::BLOCK_ELEMS;
-  const dim3 grid(stage_blocks(total), (unsigned)batch);
+  // one workgroup per destination block; every block, padding included, is written
+  const dim3 grid((unsigned)arblk::row_tiles(C), (unsigned)nkb, (unsigned)batch);
+  const int epc = 16 / elem_bytes;
+  const int vec = C % epc == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+                  ((R * C * elem_bytes) & 15) == 0;
   if (elem_bytes == 2)
     hipLaunchKernelGGL(k_block_transpose<uint16_t>, grid, dim3(NT), 0, st,
                        static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C, nkb,
-                       R * C, dst_batch);
+                       R * C, dst_batch, vec);
   else
     hipLaunchKernelGGL(k_block_transpose<uint32_t>, grid, dim3(NT), 0, st,
                        static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), R, C, nkb,
-                       R * C, dst_batch);
+                       R * C, dst_batch, vec);
   return last_status();
 }
 
