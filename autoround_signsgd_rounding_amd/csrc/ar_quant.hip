@@ -243,18 +243,24 @@ __global__ __launch_bounds__(NT) void k_fill_f32(float* p, float v, int64_t n) {
 
 // ------------------------------------------------------------------ GEMM operand staging
 // Row-major src [R, KR] (row stride KR) -> blocked dst (rows R, reduction KR),
-// zero padding to whole blocks; one thread per 8-element chunk of dst.
+// zero padding to whole blocks. One workgroup per 256 rows x 64 reduction
+// elements (two blocks): eight lanes read a row's 128 bytes, and the 8 rows of
+// one instruction land as two 512-byte runs, one per block.
 __global__ __launch_bounds__(NT) void k_block_copy(const uint16_t* __restrict__ src,
                                                    uint16_t* __restrict__ dst, int64_t R,
                                                    int64_t KR, int64_t nkb, int64_t src_batch,
                                                    int64_t dst_batch) {
-  const int64_t cpr = nkb * (arblk::KB / 8);                 // chunks per padded row
-  const int64_t total = arblk::row_tiles(R) * arblk::ROWS * cpr;
+  const int64_t npair = (nkb + 1) / 2;
+  const int64_t rt = blockIdx.x / npair, kp = blockIdx.x - rt * npair;
   const int64_t b = blockIdx.y;
   src += b * src_batch;
   dst += b * dst_batch;
-  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < total; i += (int64_t)gridDim.x * NT) {
-    const int64_t r = i / cpr, k = (i - r * cpr) * 8;
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int local = it * NT + threadIdx.x;          // 0 .. 2047
+    const int64_t r = rt * arblk::ROWS + (local >> 3);
+    const int64_t k = kp * 2 * arblk::KB + (local & 7) * 8;
+    if (k >= nkb * arblk::KB) continue;               // odd nkb: the pair's second block is absent
     u32x4_t v = {0u, 0u, 0u, 0u};
     if (r < R && k < KR) v = *reinterpret_cast<const u32x4_t*>(src + r * KR + k);
     *reinterpret_cast<u32x4_t*>(dst + arblk::chunk_offset(r, k, nkb)) = v;
@@ -596,9 +602,11 @@ static unsigned stage_blocks(int64_t total) {
 
 ar_status ar_launch_block_copy(const uint16_t* src, uint16_t* dst, int64_t batch, int64_t R,
                                int64_t KR, int64_t nkb, hipStream_t st) {
-  const int64_t total = arblk::row_tiles(R) * arblk::ROWS * nkb * (arblk::KB / 8);
-  hipLaunchKernelGGL(k_block_copy, dim3(stage_blocks(total), (unsigned)batch), dim3(NT), 0, st,
-                     src, dst, R, KR, nkb, R * KR, arblk::row_tiles(R) * nkb * arblk::BLOCK_ELEMS);
+  if (batch <= 0 || R <= 0 || nkb <= 0) return AR_OK;
+  const int64_t wgs = arblk::row_tiles(R) * ((nkb + 1) / 2);
+  if (wgs > 0x7FFFFFFF || batch > 65535) return AR_ERR_SHAPE;
+  hipLaunchKernelGGL(k_block_copy, dim3((unsigned)wgs, (unsigned)batch), dim3(NT), 0, st, src,
+                     dst, R, KR, nkb, R * KR, arblk::row_tiles(R) * nkb * arblk::BLOCK_ELEMS);
   return last_status();
 }
 
