@@ -595,11 +595,6 @@ ar_status ar_launch_init_clip(int wdt, const void* W, int64_t N, int64_t K, int 
                         : init_make<float>(W, N, K, g, gr, init, alpha, beta, st);
 }
 
-static unsigned stage_blocks(int64_t total) {
-  const int64_t want = (total + NT - 1) / NT;
-  return (unsigned)(want < 65536 ? want : 65536);
-}
-
 ar_status ar_launch_block_copy(const uint16_t* src, uint16_t* dst, int64_t batch, int64_t R,
                                int64_t KR, int64_t nkb, hipStream_t st) {
   if (batch <= 0 || R <= 0 || nkb <= 0) return AR_OK;
