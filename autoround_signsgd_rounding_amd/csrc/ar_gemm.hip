@@ -23,6 +23,8 @@
 #include "ar_launch.h"
 #include "ar_loss.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = arblk::KB, NTHR = 256, NSTAGE = 4;
@@ -271,6 +273,331 @@ struct EpiFwdBf16 {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Streamed forward product (bf16 targets, reduction of at least FS_MIN_NK steps).
+//
+// Same tiles, operands, accumulators and per-tile arithmetic as k_gemm with
+// EpiFwdBf16, but each workgroup runs a fixed sequence of tiles:
+// u = blockIdx.x + r * gridDim.x for r = 0, 1, ..., mapped by tile_of exactly as
+// the one-tile-per-workgroup launch maps workgroup u, so XCD placement and
+// panel sharing are unchanged. What changes is when the epilogue traffic moves.
+// Per lane, the 256 targets/residuals of its 128 x 128 sub-tile sit in 64
+// slots of four bf16 tokens (the accumulator order, 8 bytes of one blocked row
+// each): the slots of accumulator blocks 0..12 in registers, those of blocks
+// 13..15 in a per-wave LDS area past the stages (two dwords per slot at
+// base + 4*lane, the layout of a 4-byte global->LDS load), which keeps the
+// kernel within 256 VGPRs. The main loop of tile r is cut into 16 groups; at the
+// start of group g the four slots of block g are first stored as tile r-1's dYᵀ
+// and then reloaded with tile r's targets (LDS slots: read back, stored, then
+// refilled by global->LDS loads). The target reads and residual writes therefore
+// run under the MFMAs instead of as a chip-wide burst after every tile, and the
+// last four steps of tile r fill the stages with tile r+1's first four steps.
+// Only the last tile's residuals leave in a burst.
+//
+// vmcnt accounting: a step waits for at most 16 outstanding vector-memory
+// operations. The newest 16 always come after the loads of step kt+1 (steps kt+2
+// and kt+3 alone are 16 loads; the slot stores and loads only add to that), and
+// the counter retires in issue order, so step kt+1's stage is complete.
+constexpr int FS_GROUPS = 16;
+constexpr int FS_MIN_NK = FS_GROUPS + NSTAGE;   // at least one main-loop step per group
+constexpr int FS_REG_G = 13;                     // blocks whose slots live in registers
+constexpr int FS_WAVE_LDS = (FS_GROUPS - FS_REG_G) * 4 * 2 * 256;   // 6 KiB per wave
+constexpr int FS_RED = LDS_BYTES + 4 * FS_WAVE_LDS;                // per-wave sums
+constexpr int FS_LDS_TOTAL = FS_RED + 64;
+static_assert(FS_LDS_TOTAL <= 160 * 1024, "LDS of one workgroup");
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// wave_sum64's butterfly (partners lane^32, ^16, ..., ^1, each lane adding its
+// partner to its own value) without lane-address registers: v_permlane32_swap for
+// the two halves, ds_swizzle xor patterns inside them. Of the swap's two results one
+// is the lane's own value and the other its partner, so x ^ r0 ^ r1 is the partner.
+__device__ __forceinline__ float wave_sum64_swz(float x) {
+  const uint32_t xb = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(xb, xb, false, false);
+  x += __uint_as_float(xb ^ (uint32_t)r[0] ^ (uint32_t)r[1]);
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (16 << 10)));
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (8 << 10)));
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (4 << 10)));
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (2 << 10)));
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (1 << 10)));
+  return x;
+}
+
+struct FwdStreamArgs {
+  const uint16_t* P;    // X_b, blocked (rows t)
+  const uint16_t* Q;    // Ŵ, blocked (rows n)
+  const uint16_t* yB;   // targets, blocked like dYᵀ (rows n, reduction t)
+  uint16_t* dyB;
+  float* partials;      // one per tile, ti * tilesJ + tj
+  int nkb, tilesI, tilesJ, nkbT, ntiles;
+};
+
+__global__ __launch_bounds__(NTHR, 1) void k_fwd_stream(FwdStreamArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[FS_LDS_TOTAL];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wi = wave >> 1, wj = wave & 1;
+  const int nk = a.nkb;
+  constexpr uint32_t TILE_BYTES = 8u * arblk::BLOCK_BYTES;   // one tile of targets / dYᵀ
+  auto tile_at = [&](int r, int& ti, int& tj) -> bool {
+    const int u = (int)blockIdx.x + r * (int)gridDim.x;
+    if (u >= a.ntiles) return false;
+    tile_of(u, a.ntiles, a.tilesI, a.tilesJ, ti, tj);
+    return true;
+  };
+  auto rsrcP = [&](int ti) {
+    return make_rsrc(a.P + (int64_t)ti * nk * arblk::BLOCK_ELEMS, (uint32_t)nk * OPB);
+  };
+  auto rsrcQ = [&](int tj) {
+    return make_rsrc(a.Q + (int64_t)tj * nk * arblk::BLOCK_ELEMS, (uint32_t)nk * OPB);
+  };
+  auto tile_off = [&](int ti, int tj) -> int64_t {
+    return ((int64_t)tj * a.nkbT + (int64_t)ti * (BM / BK)) * arblk::BLOCK_ELEMS;
+  };
+
+#define AR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+  // stage loads: piece j (0..LPI-1) of step `s` of a tile, into LDS stage `stg`
+  const uint32_t lane_off = (uint32_t)(wave * IPW * 1024 + lane * 16);
+  auto issue = [&](__amdgpu_buffer_rsrc_t bp, __amdgpu_buffer_rsrc_t bq, int stg, int s, int j) {
+    uint8_t* dst = lds + stg * STAGE_BYTES + ((j & 1) ? OPB : 0) + (wave * IPW + (j >> 1)) * 1024;
+    const uint32_t vo = lane_off + (uint32_t)(j >> 1) * 1024u;
+    const uint32_t so = (uint32_t)s * OPB;
+    if (j & 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(bq, AR_LDS(dst), 16, vo, so, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(bp, AR_LDS(dst), 16, vo, so, 0, 0);
+  };
+
+  const uint32_t rdP = (uint32_t)(wi * 128 + (lane & 31)) * ROWB;
+  const uint32_t rdQ = OPB + (uint32_t)(wj * 128 + (lane & 31)) * ROWB;
+  const int sw = ((lane & 31) >> 2) & 3, rhi = lane >> 5;
+  bf16x8_t pf[2][4], qf[2][4];
+  auto rd = [&](int stg, int ks, int buf, int idx) {
+    const uint8_t* s = lds + stg * STAGE_BYTES;
+    const uint32_t ch = (uint32_t)(((2 * ks + rhi) ^ sw) << 4);
+    const int b = idx & 3;
+    if (idx < 4) pf[buf][b] = *reinterpret_cast<const bf16x8_t*>(s + rdP + b * 32 * ROWB + ch);
+    else qf[buf][b] = *reinterpret_cast<const bf16x8_t*>(s + rdQ + b * 32 * ROWB + ch);
+  };
+
+  // register slots: slot 4*g + q holds tokens 8q + 4*(lane>>5) .. +3 of accumulator
+  // block g = 4*bj + bi; its byte offset in the tile's blocked region is the lane part
+  // qv[q] (a VGPR per q) plus the block part blk_so(g) (the instruction's scalar offset)
+  const uint32_t lane_base =
+      (uint32_t)(wi * 4 * arblk::BLOCK_BYTES + (wj * 128 + (lane & 31)) * ROWB + (lane >> 5) * 8);
+  uint32_t qv[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) qv[q] = lane_base + ((uint32_t)(q ^ sw) << 4);
+  auto blk_so = [](int g) -> uint32_t {
+    return (uint32_t)((g & 3) * arblk::BLOCK_BYTES + (g >> 2) * 32 * ROWB);
+  };
+  u32x2_t slot[4 * FS_REG_G];
+#pragma unroll
+  for (int i = 0; i < 4 * FS_REG_G; ++i) slot[i] = u32x2_t{0u, 0u};
+  // LDS slot (block g >= FS_REG_G, q): low dwords of the wave's 64 lanes, then the high ones
+  auto lslot = [&](int g, int q) -> uint8_t* {
+    return lds + LDS_BYTES + wave * FS_WAVE_LDS + ((g - FS_REG_G) * 4 + q) * 512;
+  };
+  auto lds_get = [&](int g, int q) -> u32x2_t {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(lslot(g, q)) + lane;
+    return u32x2_t{p[0], p[64]};
+  };
+  auto lds_put = [&](int g, int q, u32x2_t v) {
+    uint32_t* p = reinterpret_cast<uint32_t*>(lslot(g, q)) + lane;
+    p[0] = v[0];
+    p[64] = v[1];
+  };
+
+  f32x16_t acc[4][4];
+  float* red = reinterpret_cast<float*>(lds + FS_RED);
+
+  int ti, tj;
+  tile_at(0, ti, tj);   // gridDim.x <= ntiles
+  __amdgpu_buffer_rsrc_t bP = rsrcP(ti), bQ = rsrcQ(tj);
+  // residuals pending from the previous tile (none before the first: every store drops)
+  __amdgpu_buffer_rsrc_t bOut = make_rsrc(a.dyB, 0u);
+  int stg0 = 0;   // stage of the current tile's step 0
+
+#pragma unroll
+  for (int s = 0; s < NSTAGE; ++s)
+#pragma unroll
+    for (int j = 0; j < LPI; ++j) issue(bP, bQ, s, s, j);
+  wait_vm((NSTAGE - 1) * LPI);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int idx = 0; idx < 8; ++idx) rd(0, 0, 0, idx);
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int r = 0;; ++r) {
+    int nti = ti, ntj = tj;
+    const bool more = tile_at(r + 1, nti, ntj);
+    // without a next tile the tail refills read an empty range (zeros into stages nobody reads)
+    const __amdgpu_buffer_rsrc_t nP = more ? rsrcP(nti) : make_rsrc(a.P, 0u);
+    const __amdgpu_buffer_rsrc_t nQ = more ? rsrcQ(ntj) : make_rsrc(a.Q, 0u);
+    const __amdgpu_buffer_rsrc_t bY = make_rsrc(a.yB + tile_off(ti, tj), TILE_BYTES);
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.0f;
+
+    // one step: as in k_gemm; the refill of stage kt takes step kt+4 of this tile
+    // (tail = false) or step kt+4-nk of the next tile (tail = true). The tile's last
+    // step (last = true) leaves the next tile's first fragments for after the epilogue,
+    // so that they are not held in registers through it.
+    auto step = [&](int kt, bool tail, bool last = false) {
+      const int sc = (stg0 + kt) & (NSTAGE - 1), sn = (sc + 1) & (NSTAGE - 1);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        acc[m >> 2][m & 3] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[0][m >> 2], qf[0][m & 3], acc[m >> 2][m & 3], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (m & 1) {
+          rd(sc, 1, 1, m >> 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      wait_vm((NSTAGE - 2) * LPI);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        acc[m >> 2][m & 3] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[1][m >> 2], qf[1][m & 3], acc[m >> 2][m & 3], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (m & 1) {
+          if (!last) rd(sn, 0, 0, m >> 1);
+        } else if (tail) issue(nP, nQ, sc, kt + NSTAGE - nk, m >> 1);
+        else issue(bP, bQ, sc, kt + NSTAGE, m >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    const int S = (nk - NSTAGE) / FS_GROUPS;   // >= 1 (nk >= FS_MIN_NK)
+    __builtin_assume(S >= 1);
+    int kt = 0;
+#pragma unroll
+    for (int g = 0; g < FS_GROUPS; ++g) {
+      // the previous tile's residuals of block g out, this tile's targets of block g in
+      if (g < FS_REG_G) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          __builtin_amdgcn_raw_buffer_store_b64(slot[4 * g + q], bOut, qv[q], blk_so(g), 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          slot[4 * g + q] = __builtin_amdgcn_raw_buffer_load_b64(bY, qv[q], blk_so(g), 0);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          __builtin_amdgcn_raw_buffer_store_b64(lds_get(g, q), bOut, qv[q], blk_so(g), 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // (the reads above have returned: the stores consumed their data)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bY, AR_LDS(lslot(g, q)), 4, qv[q], blk_so(g), 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bY, AR_LDS(lslot(g, q) + 256), 4, qv[q],
+                                                   blk_so(g) + 4u, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      int j = 0;
+      do {
+        step(kt, false);
+        ++kt;
+      } while (++j < S);
+    }
+    for (; kt < nk - NSTAGE; ++kt) step(kt, false);
+#pragma unroll
+    for (int t = 0; t < NSTAGE; ++t) step(nk - NSTAGE + t, true, t == NSTAGE - 1);
+
+    // R = Y' - Y_true in place of the targets, tile's sum of R² in the order of EpiFwdBf16.
+    // The LDS slots' target loads are complete: they were issued before the tail steps'
+    // 32 loads, and the last step waited until at most 16 operations were outstanding.
+    __builtin_amdgcn_sched_barrier(0);
+    float sq = 0.0f;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int g = 4 * bj + bi;
+          u32x2_t v = g < FS_REG_G ? slot[4 * g + q] : lds_get(g, q);
+          const float y[4] = {__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
+                              __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
+          float rr[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            rr[e] = acc[bi][bj][q * 4 + e] - y[e];
+            sq += rr[e] * rr[e];
+          }
+          // v_cvt_pk_bf16_f32: nearest-even, the same bits as bf16_bits for every
+          // non-NaN value (NaN stays NaN, payload aside); no per-element compare
+          const bf16x2_t h0 = {(__bf16)rr[0], (__bf16)rr[1]};
+          const bf16x2_t h1 = {(__bf16)rr[2], (__bf16)rr[3]};
+          v[0] = __builtin_bit_cast(uint32_t, h0);
+          v[1] = __builtin_bit_cast(uint32_t, h1);
+          if (g < FS_REG_G) slot[4 * g + q] = v;
+          else lds_put(g, q, v);
+          __builtin_amdgcn_sched_barrier(0);   // one slot's temporaries live at a time
+        }
+    sq = wave_sum64_swz(sq);
+    if (lane == 0) red[wave] = sq;
+    // The sums pass through LDS only: wait for this wave's LDS write, then the barrier,
+    // with compiler-only memory clobbers around it. A fence would also wait for the
+    // next tile's global->LDS stage loads (vmcnt), which must stay in flight here.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (wave == 0 && lane == 0) a.partials[ti * a.tilesJ + tj] = ((red[0] + red[1]) + red[2]) + red[3];
+    bOut = make_rsrc(a.dyB + tile_off(ti, tj), TILE_BYTES);
+    if (!more) break;
+    ti = nti; tj = ntj; bP = nP; bQ = nQ;
+    stg0 = (stg0 + nk) & (NSTAGE - 1);
+    // next tile's step 0 (stage complete and visible: the last step's wait and barrier)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int idx = 0; idx < 8; ++idx) rd(stg0, 0, 0, idx);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // the last tile's residuals
+#pragma unroll
+  for (int g = 0; g < FS_GROUPS; ++g)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_buffer_store_b64(g < FS_REG_G ? slot[4 * g + q] : lds_get(g, q), bOut,
+                                            qv[q], blk_so(g), 0);
+#undef AR_LDS
+}
+
+// Workgroups the streamed forward product keeps resident: one per compute unit
+// (its LDS allows no more), a multiple of 8 so that workgroup w's tiles stay on
+// XCD w mod 8. Remembered per device.
+int fwd_stream_grid(int ntiles) {
+  static std::mutex mu;
+  static int cus_of[64] = {0};
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    cus = 256;
+  } else {
+    std::lock_guard<std::mutex> lk(mu);
+    if (cus_of[dev] == 0) {
+      int c = 0;
+      if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) {
+        (void)hipGetLastError();
+        c = 256;
+      }
+      cus_of[dev] = c;
+    }
+    cus = cus_of[dev];
+  }
+  int g = cus >= 8 ? cus / 8 * 8 : cus;
+  return ntiles < g ? ntiles : g;
+}
+
 // float32 targets (float32 layers): read straight from the blocked array.
 struct EpiFwdF32 {
   static constexpr int kPrefetch = 0;
@@ -370,7 +697,11 @@ ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void*
   a.tilesJ = (int)arblk::row_tiles(N);
   const int nkbT = (int)(arblk::row_tiles(Tb) * (BM / BK));
   const int nwg = a.tilesI * a.tilesJ;
-  if (ydt == AR_BF16) {
+  if (ydt == AR_BF16 && a.nkb >= FS_MIN_NK) {
+    FwdStreamArgs s{XB, WB, static_cast<const uint16_t*>(yB), dyB, partials,
+                    a.nkb, a.tilesI, a.tilesJ, nkbT, nwg};
+    hipLaunchKernelGGL(k_fwd_stream, dim3(fwd_stream_grid(nwg)), dim3(NTHR), 0, st, s);
+  } else if (ydt == AR_BF16) {
     EpiFwdBf16 e{static_cast<const uint16_t*>(yB), dyB, partials, nkbT, a.tilesJ};
     hipLaunchKernelGGL(k_gemm<EpiFwdBf16>, dim3(nwg), dim3(NTHR), 0, st, a, e);
   } else {
