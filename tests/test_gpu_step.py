@@ -52,6 +52,9 @@ STEP_CASES = [
     (520, 200, 136, "bf16", "f32", 8, 40, False, None),     # ragged K and Tb reductions
     (100, 1024, 1032, "bf16", "bf16", 4, 1024, False, 0.0), # frozen clip factors
     (1, 64, 8, "f32", "f32", 4, 64, True, None),            # one row, one 8-token batch
+    # ragged N and Tb over 17 x 17 = 289 forward tiles: with one workgroup per CU some run a
+    # second tile; K = 640 is the shortest reduction the streamed forward takes (20 steps)
+    (4100, 640, 4104, "bf16", "bf16", 4, 128, False, None),
 ]
 
 
