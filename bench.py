@@ -23,6 +23,7 @@ import os
 import platform
 import sys
 import time
+import types
 
 import numpy as np
 
@@ -268,6 +269,25 @@ def _pack_time(ar, torch, out, bits, reps=20):
     return e0.elapsed_time(e1) / (5 * reps)
 
 
+def _pack_large(ar, torch, N=29568, K=8192, bits=4, g=128):
+    """ar_pack on a Qwen2.5-72B up_proj-sized layer (random codes and
+    zero-points of the grid; the speed does not depend on their values),
+    graph-timed as above: N·K code bytes in, N·K·bits/8 packed bytes out, plus
+    the zero-points."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    G = K // g
+    hi = 1 << bits
+    codes = torch.randint(0, hi, (N, K), dtype=torch.uint8, device=dev, generator=gen)
+    zp = torch.randint(0, hi, (N, G), dtype=torch.uint8, device=dev, generator=gen)
+    ms = _pack_time(ar, torch, types.SimpleNamespace(codes=codes, zp=zp), bits)
+    nbytes = N * K + N * K * bits // 8 + N * G * (1 + bits / 8)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"shape": f"W{bits} g{g} {N}x{K}", "ms": round(ms, 4), "GB/s": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": int(nbytes)}
+
+
 def _block_run(ar, torch, iters=200):
     """Sequential block-wise tuning with quantized inputs (ar_tune_block) of a
     Llama-7B-shaped decoder block (D 4096, 32 heads, F 11008) on 16 synthetic
@@ -496,6 +516,7 @@ def main():
             "pack_timing": "HIP graph of 20 ar_pack calls on the tuned codes, replayed",
             "pack_gbps": round(pack_bytes / (pack_ms * 1e-3) / 1e9, 1),
             "pack_hbm_frac": round(pack_bytes / (pack_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "pack_large": _pack_large(ar, torch),
             "best_loss": final_loss,
             "input_gen_s": round(t_gen, 1),
         },
