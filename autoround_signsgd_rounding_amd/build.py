@@ -6,6 +6,7 @@
 loads the library being built).
 """
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -28,16 +29,43 @@ FLAGS = [
 ]
 
 
+# Kernels whose speed depends on running without register spills: the MFMA
+# contractions sit at the register file's limit. A spill (to scratch memory,
+# behind a full vector-memory wait) is reported as a warning.
+HOT = ("k_fwd_stream", "k_gemm", "k_dq_mfma", "k_attention")
+_FN = re.compile(r"Function Name: (\S+)")
+_SPILL = re.compile(r"VGPRs Spill: (\d+)")
+
+
+def _spills(remarks):
+    out, fn = [], None
+    for ln in remarks:
+        m = _FN.search(ln)
+        if m:
+            fn = m.group(1)
+            continue
+        m = _SPILL.search(ln)
+        if m and fn and int(m.group(1)) > 0 and any(h in fn for h in HOT):
+            out.append((fn, int(m.group(1))))
+    return out
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (r.stderr or "").splitlines() if noise not in ln and ln.strip()]
+    lines = (r.stderr or "").splitlines()
+    remarks = [ln for ln in lines if "kernel-resource-usage" in ln]
+    msgs = [ln for ln in lines if noise not in ln and ("warning:" in ln or "error:" in ln)]
     if msgs:
         print("\n".join(msgs), file=sys.stderr)
+    for fn, n in _spills(remarks):
+        print(f"warning: {src}: {fn} spills {n} VGPRs (scratch traffic in a hot loop)",
+              file=sys.stderr)
     return obj
 
 
