@@ -18,6 +18,13 @@
 // the first fragments of the next step are read while the second substep's
 // MFMAs run. Fragments are double-buffered in registers and every MFMA is
 // followed by at most one LDS read or one global load (explicit order).
+//
+// Two kernels share that step. k_gemm runs one tile per workgroup with a
+// pluggable epilogue (forward with float32 targets or short reductions, the
+// weight gradient, the Gram-form product, the plain product).
+// k_fwd_stream is the forward with bf16 targets: one workgroup per CU runs its
+// tiles in turn and moves the targets and residuals under the MFMAs. Both
+// produce the same bits.
 #include "ar_blocked.h"
 #include "ar_device.h"
 #include "ar_launch.h"
