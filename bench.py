@@ -40,11 +40,22 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_gemm_llama7b_q_proj.t
 GEMM_SOURCE = os.path.join(ROOT, "autoround_signsgd_rounding_amd", "csrc", "ar_gemm.hip")
 
 
+def gemm_code_hash(path=GEMM_SOURCE):
+    """sha256 of the GEMM source's code: comments removed and whitespace
+    collapsed, so that an edit of comments alone keeps the counters valid."""
+    import hashlib
+    import re
+    text = open(path, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode("utf-8")).hexdigest()
+
+
 def _measured_traffic(workload):
     """HBM bytes per launch of the forward GEMM from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE runs, or None when they were taken on another
-    workload or the GEMM source has changed since."""
-    import hashlib
+    workload or the GEMM code has changed since."""
     if workload != "llama7b_q_proj" or not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -52,8 +63,7 @@ def _measured_traffic(workload):
         if "=" in line and not line.startswith("#"):
             k, v = line.strip().split("=", 1)
             kv[k.strip()] = v.strip()
-    src = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-    if kv.get("gemm_source_sha256") != src:
+    if kv.get("gemm_code_sha256") != gemm_code_hash():
         return None
     return int(float(kv["traffic_bytes"]))
 
