@@ -185,16 +185,22 @@ LoopWs carve_loop(void* ws, int64_t N, int64_t K, int64_t nb, int64_t Tb, int64_
 // Gram form: blocked element counts and workspace.
 struct GramSizes {
   int nred;              // 1 (bf16 W) or 2 (float32 W as W_hi + W_lo) reduction segments of K
-  int64_t nkbR, nkb3;    // k-blocks of the statistics product (nred·K) and of D·H (3K)
+  int64_t nkbR;          // k-blocks of the statistics product (nred·K)
+  // D·H runs over three parts of Kp = K rounded up to whole k-blocks: H is stored
+  // [H_hi | H_lo | H_hi] (nkbH k-blocks), D as [D_hi | D_lo] (nkbD), the product
+  // reading D's first part for both of H's first two.
+  int64_t Kp, nkbH, nkbD;
   int64_t xb2, wb2, hb, db, fsz;
   GramSizes(int wdt, int64_t N, int64_t K, int64_t Tb) {
     nred = wdt == AR_F32 ? 2 : 1;
     nkbR = arblk::k_blocks(nred * K);
-    nkb3 = arblk::k_blocks(3 * K);
+    Kp = arblk::k_blocks(K) * arblk::KB;
+    nkbH = 3 * arblk::k_blocks(K);
+    nkbD = 2 * arblk::k_blocks(K);
     xb2 = arblk::row_tiles(Tb) * nkbR * arblk::BLOCK_ELEMS;
     wb2 = arblk::row_tiles(N) * nkbR * arblk::BLOCK_ELEMS;
-    hb = arblk::row_tiles(K) * nkb3 * arblk::BLOCK_ELEMS;
-    db = arblk::row_tiles(N) * nkb3 * arblk::BLOCK_ELEMS;
+    hb = arblk::row_tiles(K) * nkbH * arblk::BLOCK_ELEMS;
+    db = arblk::row_tiles(N) * nkbD * arblk::BLOCK_ELEMS;
     fsz = (N > K ? N : K) * K;
   }
 };
@@ -210,7 +216,7 @@ struct GramWs {
   uint16_t* WB2;   // [W] or [W_hi | W_lo], rows N
   float* F;        // H of a minibatch (staging), then P = D·H (loop)
   float* fwd_partials;
-  uint16_t* DB;    // [D_hi | D_hi | D_lo], rows N
+  uint16_t* DB;    // [D_hi | D_lo], rows N
   float *V[2], *A[2], *B[2];
   float *bestV, *bestA, *bestB;
   float* partials;
@@ -329,9 +335,9 @@ ar_status stage_gram_minibatch(const GramWs& w, const GramSizes& q, int64_t N, i
   // H = X_bᵀ·X_b, then its hi/lo operand [H_hi | H_lo | H_hi]
   ArLossIn none{};
   AR_TRY(ar_launch_gemm_f32out(XTBb, XTBb, w.F, K, K, nkbT, 1.0f, none, st));
-  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkb3, 0, 0, st));
-  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkb3, K, 1, st));
-  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkb3, 2 * K, 0, st));
+  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkbH, 0, 0, st));
+  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkbH, q.Kp, 1, st));
+  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkbH, 2 * q.Kp, 0, st));
   return AR_OK;
 }
 

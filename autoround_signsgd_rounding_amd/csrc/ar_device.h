@@ -21,6 +21,15 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
 }
 __device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Two values to bf16 in one v_cvt_pk_bf16_f32 (lo in bits 0..15): nearest
+// even, the same bits as bf16_bits for every non-NaN value (a NaN stays a
+// NaN, its payload aside).
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  const bf16x2_hw_t h = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // ---------------------------------------------------------------- buffer resources
 // Raw buffer descriptor: loads at byte offsets >= num_bytes return zero, which
 // gives free zero-fill for ragged tiles (rows past the end of a panel).

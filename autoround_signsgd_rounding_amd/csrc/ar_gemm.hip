@@ -73,10 +73,13 @@ __device__ __forceinline__ void tile_of(int w, int nwg, int tilesI, int tilesJ, 
 }
 
 struct GemmArgs {
-  const uint16_t* P;   // blocked, tilesI panels of nkb blocks
+  const uint16_t* P;   // blocked, tilesI panels of nkb blocks (nkP with a folded P)
   const uint16_t* Q;   // blocked, tilesJ panels of nkb blocks
   int nkb;
   int tilesI, tilesJ;
+  // Folded P (epilogues with kFoldP): P panels hold nkP blocks and reduction
+  // step kt reads P block kt for kt < foldP, else kt - foldP.
+  int nkP = 0, foldP = 0;
 };
 
 template <class Epi>
@@ -88,8 +91,9 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
   int ti, tj;
   tile_of(blockIdx.x, gridDim.x, a.tilesI, a.tilesJ, ti, tj);
   const int nk = a.nkb;
+  const int nkP = Epi::kFoldP ? a.nkP : nk;
   const __amdgpu_buffer_rsrc_t bufP =
-      make_rsrc(a.P + (int64_t)ti * nk * arblk::BLOCK_ELEMS, (uint32_t)nk * OPB);
+      make_rsrc(a.P + (int64_t)ti * nkP * arblk::BLOCK_ELEMS, (uint32_t)nkP * OPB);
   const __amdgpu_buffer_rsrc_t bufQ =
       make_rsrc(a.Q + (int64_t)tj * nk * arblk::BLOCK_ELEMS, (uint32_t)nk * OPB);
 
@@ -102,10 +106,12 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
   auto issue_main = [&](int kt, int j) {   // kt < nk
     const uint32_t vo = lane_off + (uint32_t)(j >> 1) * 1024u;
     const uint32_t so = (uint32_t)kt * OPB;
-    if (j & 1)
+    if (j & 1) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(bufQ, AR_LDS(lds_dst(kt, j)), 16, vo, so, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(bufP, AR_LDS(lds_dst(kt, j)), 16, vo, so, 0, 0);
+    } else {
+      const uint32_t sp = Epi::kFoldP && kt >= a.foldP ? (uint32_t)(kt - a.foldP) * OPB : so;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bufP, AR_LDS(lds_dst(kt, j)), 16, vo, sp, 0, 0);
+    }
   };
   // kt >= nk: the freed stage takes piece kt-nk of the epilogue's prefetch (piece j lands
   // in stage (nk + j) % NSTAGE); without a prefetch, an out-of-range load keeps the
@@ -210,6 +216,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm(GemmArgs a, Epi epi) {
 // coalesced stores.
 struct EpiFwdBf16 {
   static constexpr int kPrefetch = NSTAGE;     // 4 x 32 KiB = the whole target tile
+  static constexpr bool kFoldP = false;
   const uint16_t* yB;   // targets, blocked like dYᵀ (rows n, reduction t)
   uint16_t* dyB;
   float* partials;
@@ -608,6 +615,7 @@ int fwd_stream_grid(int ntiles) {
 // float32 targets (float32 layers): read straight from the blocked array.
 struct EpiFwdF32 {
   static constexpr int kPrefetch = 0;
+  static constexpr bool kFoldP = false;
   const float* yB;
   uint16_t* dyB;
   float* partials;
@@ -663,6 +671,7 @@ __device__ __forceinline__ void loss_pre(const ArLossIn& L, uint8_t* extra) {
 // out[i, j] = scale * acc, rows i < N, columns j < K of a row-major [N, K].
 struct EpiWgrad {
   static constexpr int kPrefetch = 0;
+  static constexpr bool kFoldP = false;
   float* G;   // [N, K] row-major
   int64_t N, K;
   float scale;
@@ -722,6 +731,7 @@ ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void*
 // i < M (rows of P), j < N (rows of Q), row-major, float32 or bf16.
 struct EpiOut {
   static constexpr int kPrefetch = 0;
+  static constexpr bool kFoldP = false;
   void* Y;
   int64_t M, N;
   int ydt;
@@ -765,17 +775,21 @@ ar_status ar_launch_gemm_out(const uint16_t* XB, const uint16_t* WB, void* Y, in
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
 
-// The Gram-form product D·H gets its own type so that profiles name it apart
-// from the weight-gradient product (same code).
-struct EpiGramP : EpiWgrad {};
+// The Gram-form product D·H: the weight-gradient epilogue, with D folded (D is
+// stored [D_hi | D_lo] against H's [H_hi | H_lo | H_hi]). Its own type also
+// names it apart in profiles.
+struct EpiGramP : EpiWgrad {
+  static constexpr bool kFoldP = true;
+};
 
 template <class Epi>
 static ar_status launch_f32out(const uint16_t* P, const uint16_t* Q, float* out, int64_t rowsP,
                                int64_t rowsQ, int64_t nkb, float scale, const ArLossIn& loss,
-                               hipStream_t st) {
+                               hipStream_t st, int64_t nkP = 0, int64_t foldP = 0) {
   GemmArgs a;
   a.P = P; a.Q = Q;
   a.nkb = (int)nkb;
+  a.nkP = (int)nkP; a.foldP = (int)foldP;
   a.tilesI = (int)arblk::row_tiles(rowsP);
   a.tilesJ = (int)arblk::row_tiles(rowsQ);
   Epi e;
@@ -792,7 +806,9 @@ ar_status ar_launch_gemm_f32out(const uint16_t* P, const uint16_t* Q, float* out
 
 ar_status ar_launch_gemm_gram(const uint16_t* DB, const uint16_t* HB, float* P, int64_t N,
                               int64_t K, const ArLossIn& loss, hipStream_t st) {
-  return launch_f32out<EpiGramP>(DB, HB, P, N, K, arblk::k_blocks(3 * K), 1.0f, loss, st);
+  // reduction over [H_hi | H_lo | H_hi] (3 parts of k_blocks(K) blocks); D = [D_hi | D_lo]
+  const int64_t kb = arblk::k_blocks(K);
+  return launch_f32out<EpiGramP>(DB, HB, P, N, K, 3 * kb, 1.0f, loss, st, 2 * kb, kb);
 }
 
 ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* G, int64_t N,

@@ -58,21 +58,22 @@ __global__ __launch_bounds__(NT) void k_place(const T* __restrict__ src, uint16_
   }
 }
 
-// D = bf16(Ŵ) − W of one chunk, split and stored as [D_hi | D_hi | D_lo].
-__device__ __forceinline__ void store_d(uint16_t* DB, int64_t nkb3, int64_t K, int64_t n,
+// D = bf16(Ŵ) − W of one chunk, split and stored as [D_hi | D_lo] (each part Kp =
+// K rounded up to whole k-blocks wide; the product reads D_hi against both H_hi
+// and H_lo).
+__device__ __forceinline__ void store_d(uint16_t* DB, int64_t nkbD, int64_t Kp, int64_t n,
                                         int64_t k, const float (&w)[8], const float (&wq)[8]) {
   u32x4_t h, l;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float d0 = bf16_val(bf16_bits(wq[2 * i])) - w[2 * i];
-    const float d1 = bf16_val(bf16_bits(wq[2 * i + 1])) - w[2 * i + 1];
-    const uint32_t h0 = bf16_bits(d0), h1 = bf16_bits(d1);
-    h[i] = h0 | (h1 << 16);
-    l[i] = bf16_bits(d0 - bf16_val(h0)) | (bf16_bits(d1 - bf16_val(h1)) << 16);
+    const uint32_t q = bf16_pair(wq[2 * i], wq[2 * i + 1]);
+    const float d0 = __uint_as_float(q << 16) - w[2 * i];
+    const float d1 = __uint_as_float(q & 0xFFFF0000u) - w[2 * i + 1];
+    h[i] = bf16_pair(d0, d1);
+    l[i] = bf16_pair(d0 - __uint_as_float(h[i] << 16), d1 - __uint_as_float(h[i] & 0xFFFF0000u));
   }
-  *reinterpret_cast<u32x4_t*>(DB + arblk::chunk_offset(n, k, nkb3)) = h;
-  *reinterpret_cast<u32x4_t*>(DB + arblk::chunk_offset(n, K + k, nkb3)) = h;
-  *reinterpret_cast<u32x4_t*>(DB + arblk::chunk_offset(n, 2 * K + k, nkb3)) = l;
+  *reinterpret_cast<u32x4_t*>(DB + arblk::chunk_offset(n, k, nkbD)) = h;
+  *reinterpret_cast<u32x4_t*>(DB + arblk::chunk_offset(n, Kp + k, nkbD)) = l;
 }
 
 // ------------------------------------------------------------------ D of a state
@@ -86,7 +87,7 @@ struct GramD {
   int g, Gn, E;
   ArGrid gr;
   uint16_t* DB;
-  int64_t nkb3;
+  int64_t nkbD, Kp;     // D's k-blocks (two parts) and the width of one part
 };
 
 template <typename WT, int LPG>
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(NT) void k_gram_d(GramD<WT> a) {
     load8(a.V + off, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) wq[i] = quant_elem(w[i], v[i], p, gr).what;
-    store_d(a.DB, a.nkb3, a.K, n, off - n * a.K, w, wq);
+    store_d(a.DB, a.nkbD, a.Kp, n, off - n * a.K, w, wq);
   }
 }
 
@@ -140,7 +141,7 @@ struct GramK {
   float* bestA;
   float* bestB;
   uint16_t* DB;          // next D operand
-  int64_t nkb3;
+  int64_t nkbD, Kp;     // D's k-blocks (two parts) and the width of one part
   float* partials;       // per workgroup: sum of D·(P + 2·Cn) over its elements
   float* gV;
   float* gA;
@@ -209,7 +210,23 @@ __global__ __launch_bounds__(NT) void k_ste_gram(GramK<WT> a) {
 
   // phase 2: gradient, loss term, straight-through sums
   float A = 0.0f, Bs = 0.0f;
-  if (live) {
+  uint32_t mbits = 0u;   // ONE: element i's straight-through mask under p, kept for phase 3
+  if (live && ONE) {
+    // gram_grad and ste_accum fused: one quantization per element; each sum
+    // (loss term, A, Bs) still adds its terms in element order
+    float g[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const QE q = quant_elem(w0[i], v0[i], p, gr);
+      const float d = __uint_as_float(bf16_pair(q.what, 0.0f) << 16) - w0[i];
+      lsum += d * (p0[i] + 2.0f * c0[i]);
+      g[i] = (p0[i] + c0[i]) * a.scale;
+      const float dd = (q.q - p.zp) - (q.m ? q.t : 0.0f);
+      A += g[i] * dd;
+      if (!q.m) Bs += g[i];
+      mbits |= (uint32_t)q.m << i;
+    }
+  } else if (live) {
     for (int e = 0; e < E; ++e) {
       float w[8], v[8], pp[8], cc[8], g[8];
       if (ONE) {
@@ -241,7 +258,20 @@ __global__ __launch_bounds__(NT) void k_ste_gram(GramK<WT> a) {
   const QP pn = group_qparams(live ? mn : -1.0f, live ? mx : 1.0f, an, bn, gr);
 
   // phase 3: offsets, the previous state's snapshot, the next D operand
-  if (live) {
+  if (live && ONE) {
+    float g[8], gv[8], vn[8], wq[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) g[i] = (p0[i] + c0[i]) * a.scale;
+    ste_chunk_update_m(w0, v0, g, mbits, p, pn, gr, a.lr, a.apply, gv, vn, wq);
+    if (a.gV) store8(a.gV + off0, gv);
+    if (snap) {
+      float vo[8];
+      load8(a.Vn + off0, vo);
+      store8(a.bestV + off0, vo);
+    }
+    store8(a.Vn + off0, vn);
+    store_d(a.DB, a.nkbD, a.Kp, n, off0 - n * a.K, w0, wq);
+  } else if (live) {
     for (int e = 0; e < E; ++e) {
       const int64_t off = off0 + 8 * LPG * e;
       float w[8], v[8], pp[8], cc[8], g[8];
@@ -262,7 +292,7 @@ __global__ __launch_bounds__(NT) void k_ste_gram(GramK<WT> a) {
         store8(a.bestV + off, vo);
       }
       store8(a.Vn + off, vn);
-      store_d(a.DB, a.nkb3, a.K, n, off - n * a.K, w, wq);
+      store_d(a.DB, a.nkbD, a.Kp, n, off - n * a.K, w, wq);
     }
   }
 
@@ -300,7 +330,7 @@ ar_status gram_d_make(const void* W, const float* V, const float* A, const float
   int lpg, E;
   ar_group_layout(g, &lpg, &E);
   GramD<WT> a{static_cast<const WT*>(W), V, A, B, N * (K / g), K, g, (int)(K / g), E, gr, DB,
-              arblk::k_blocks(3 * K)};
+              2 * arblk::k_blocks(K), arblk::k_blocks(K) * arblk::KB};
   const unsigned nb = (unsigned)((a.ngroups * lpg + NT - 1) / NT);
   switch (lpg) {
 #define AR_GD_CASE(L) \
@@ -320,7 +350,8 @@ ar_status ste_gram_make(const ArGramArgs& s, hipStream_t st) {
   GramK<WT> a{static_cast<const WT*>(s.W), s.Vc, s.Vn, s.Ac, s.Bc, s.An, s.Bn, s.P, s.Cn,
               s.N * (s.K / s.g), s.K, s.g, (int)(s.K / s.g), E, s.gr, s.lr, s.mlr, s.clip_lo,
               s.clip_hi, s.scale, s.apply, s.flag_prev, s.bestV, s.bestA, s.bestB, s.DB,
-              arblk::k_blocks(3 * s.K), s.partials, s.gV, s.gA, s.gB};
+              2 * arblk::k_blocks(s.K), arblk::k_blocks(s.K) * arblk::KB, s.partials, s.gV, s.gA,
+              s.gB};
   const unsigned nb = (unsigned)ar_gram_partials(s.N, s.K, s.g);
   switch (lpg * 2 + (E == 1 ? 1 : 0)) {
 #define AR_SG_CASE(L)                                                                       \

@@ -77,6 +77,23 @@ __device__ __forceinline__ void ste_chunk_update(const float (&w)[8], const floa
   }
 }
 
+// The update above for a chunk whose straight-through masks m (bit i for
+// element i) were already found under p: no second quantization under p.
+__device__ __forceinline__ void ste_chunk_update_m(const float (&w)[8], const float (&v)[8],
+                                                   const float (&g)[8], uint32_t mbits,
+                                                   const QP& p, const QP& pn, const Grid& gr,
+                                                   float lr, int apply, float (&gv)[8],
+                                                   float (&vn)[8], float (&wq)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool m = (mbits >> i) & 1u;
+    gv[i] = m ? g[i] * p.s : 0.0f;
+    const float sg = m ? sgnf(g[i]) : 0.0f;
+    vn[i] = apply ? fminf(fmaxf(v[i] - lr * sg, -0.5f), 0.5f) : v[i];
+    wq[i] = quant_elem(w[i], vn[i], pn, gr).what;
+  }
+}
+
 // One step for the elements of one chunk: the update above, an optional
 // snapshot of the pre-update offset, and the bf16 fake-quant of the updated
 // state for the next forward product.
