@@ -379,14 +379,15 @@ __device__ __forceinline__ void pack_block(const uint8_t* b, uint32_t (&out)[Pac
 
 // codes [N, K] -> qweight [K*BITS/32, N] through an LDS tile of 64 rows x 256
 // codes: coalesced 16-byte loads along K (4-byte loads when K % 16 != 0), and
-// word stores coalesced along N.
+// word stores coalesced along N. (bx, by) = (256-code block along K, 64-row
+// block along N).
 constexpr int PK_ROW = 256 + 16;   // LDS bytes per tile row
 template <int BITS, bool V16>
-__global__ __launch_bounds__(NT) void k_pack_w(const uint8_t* __restrict__ codes,
-                                               uint32_t* __restrict__ qw, int64_t N, int64_t K) {
+__device__ __forceinline__ void pack_w_tile(uint8_t* tile, const uint8_t* __restrict__ codes,
+                                            uint32_t* __restrict__ qw, int64_t N, int64_t K,
+                                            int64_t bx, int64_t by) {
   using S = PackShape<BITS>;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[64 * PK_ROW];
-  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 256;
+  const int64_t n0 = by * 64, k0 = bx * 256;
   if constexpr (V16) {
     for (int i = threadIdx.x; i < 64 * 16; i += NT) {
       const int r = i >> 4, c = i & 15;
@@ -423,14 +424,14 @@ __global__ __launch_bounds__(NT) void k_pack_w(const uint8_t* __restrict__ codes
 // [group][column], then stores each group's words contiguously. When one chunk
 // holds every group, the workgroup's zero-points are one contiguous run of
 // rows·G bytes (16-byte aligned with zp: 256·G is a multiple of 16), read in
-// 16-byte pieces whatever G is.
-constexpr int PZ_G = 128;
+// 16-byte pieces whatever G is. (bx, by) = (256-column block, PZ_G-group chunk).
+constexpr int PZ_G = 64;    // groups per zero-point tile: its LDS equals the code tile's (64 rows)
 template <int BITS>
-__global__ __launch_bounds__(NT) void k_pack_z(const uint8_t* __restrict__ zp,
-                                               uint32_t* __restrict__ qz, int64_t N, int64_t G) {
+__device__ __forceinline__ void pack_z_tile(uint8_t* tile, const uint8_t* __restrict__ zp,
+                                            uint32_t* __restrict__ qz, int64_t N, int64_t G,
+                                            int64_t bx, int64_t by) {
   using S = PackShape<BITS>;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[PZ_G * PK_ROW];
-  const int64_t n0 = (int64_t)blockIdx.x * 256, j0 = (int64_t)blockIdx.y * PZ_G;
+  const int64_t n0 = bx * 256, j0 = by * PZ_G;
   const int gc = (int)(G - j0 < PZ_G ? G - j0 : PZ_G);
   const int rows = (int)(N - n0 < 256 ? N - n0 : 256);
   const int64_t words = N * BITS / 32;
@@ -473,6 +474,24 @@ __global__ __launch_bounds__(NT) void k_pack_z(const uint8_t* __restrict__ zp,
 #pragma unroll
     for (int w = 0; w < S::WB; ++w)
       qz[(j0 + jj) * words + (n0 / S::CB + blk) * S::WB + w] = out[w];
+  }
+}
+
+// Both packs in one launch (they share nothing): workgroups [0, nw) pack the
+// codes, the pack_w grid walked along K first; the rest pack the zero-points.
+template <int BITS, bool V16>
+__global__ __launch_bounds__(NT) void k_pack(const uint8_t* __restrict__ codes,
+                                             const uint8_t* __restrict__ zp,
+                                             uint32_t* __restrict__ qw, uint32_t* __restrict__ qz,
+                                             int64_t N, int64_t K, int64_t G, int64_t wx,
+                                             int64_t nw, int64_t zx) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[PZ_G * PK_ROW];
+  const int64_t b = blockIdx.x;
+  if (b < nw) {
+    pack_w_tile<BITS, V16>(tile, codes, qw, N, K, b % wx, b / wx);
+  } else {
+    const int64_t z = b - nw;
+    pack_z_tile<BITS>(tile, zp, qz, N, G, z % zx, z / zx);
   }
 }
 
@@ -641,20 +660,21 @@ ar_status ar_launch_fill_f32(float* p, float v, int64_t n, hipStream_t st) {
 
 ar_status ar_launch_pack(int bits, const uint8_t* codes, const uint8_t* zp, int64_t N, int64_t K,
                          int64_t G, int32_t* qweight, int32_t* qzeros, hipStream_t st) {
-  const dim3 gw((unsigned)((K + 255) / 256), (unsigned)((N + 63) / 64));
+  const int64_t wx = (K + 255) / 256, nw = wx * ((N + 63) / 64);
+  const int64_t zx = (N + 255) / 256, nz = zp ? zx * ((G + PZ_G - 1) / PZ_G) : 0;
+  if (nw + nz > 0x7FFFFFFF) return AR_ERR_SHAPE;
+  const dim3 grid((unsigned)(nw + nz));
   uint32_t* qw = reinterpret_cast<uint32_t*>(qweight);
   uint32_t* qz = reinterpret_cast<uint32_t*>(qzeros);
   switch (bits) {
 #define AR_PACK_CASE(B)                                                                       \
   case B:                                                                                     \
     if (K % 16 == 0)                                                                          \
-      hipLaunchKernelGGL((k_pack_w<B, true>), gw, dim3(NT), 0, st, codes, qw, N, K);          \
+      hipLaunchKernelGGL((k_pack<B, true>), grid, dim3(NT), 0, st, codes, zp, qw, qz, N, K, G, \
+                         wx, nw, zx);                                                         \
     else                                                                                      \
-      hipLaunchKernelGGL((k_pack_w<B, false>), gw, dim3(NT), 0, st, codes, qw, N, K);         \
-    if (zp)                                                                                   \
-      hipLaunchKernelGGL(k_pack_z<B>, dim3((unsigned)((N + 255) / 256),                        \
-                                           (unsigned)((G + PZ_G - 1) / PZ_G)),                 \
-                         dim3(NT), 0, st, zp, qz, N, G);                                      \
+      hipLaunchKernelGGL((k_pack<B, false>), grid, dim3(NT), 0, st, codes, zp, qw, qz, N, K,  \
+                         G, wx, nw, zx);                                                      \
     break;
     AR_PACK_CASE(2) AR_PACK_CASE(3) AR_PACK_CASE(4) AR_PACK_CASE(8)
 #undef AR_PACK_CASE
