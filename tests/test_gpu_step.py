@@ -55,6 +55,9 @@ STEP_CASES = [
     # ragged N and Tb over 17 x 17 = 289 forward tiles: with one workgroup per CU some run a
     # second tile; K = 640 is the shortest reduction the streamed forward takes (20 steps)
     (4100, 640, 4104, "bf16", "bf16", 4, 128, False, None),
+    # float32 targets take the one-tile forward (EpiFwdF32): long reductions, ragged tiles
+    (300, 1024, 520, "f32", "f32", 4, 128, False, None),
+    (260, 768, 264, "bf16", "f32", 3, 128, True, None),
 ]
 
 
