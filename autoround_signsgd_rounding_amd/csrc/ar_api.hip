@@ -481,8 +481,7 @@ ar_status ar_tune_step(const ar_config* c, const ar_state* s, const uint16_t* Xb
   const BlkSizes z(N, K, Tb);
 
   // stage the minibatch into the blocked GEMM layouts, Ŵ of the current state
-  AR_TRY(ar_launch_block_copy(Xb, w.XB, 1, Tb, K, z.nkbK, st));
-  AR_TRY(ar_launch_block_transpose(Xb, w.XTB, 1, Tb, K, z.nkbT, 2, st));
+  AR_TRY(ar_launch_stage_x(Xb, w.XTB, w.XB, 1, Tb, K, z.nkbT, z.nkbK, st));
   AR_TRY(ar_launch_block_transpose(Yb, w.YB, 1, Tb, N, z.nkbT, (int)dsize(ydt), st));
   AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(w.WB), 0.0f, z.wb / 2, st));
   AR_TRY(ar_launch_fakequant(s->wdt, s->W, s->V, s->alpha, s->beta, init_of(c), N, K, g,
@@ -541,8 +540,7 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
   } while (0)
 
   // one-time staging of every minibatch into the blocked GEMM layouts
-  AR_TRY_C(ar_launch_block_copy(X, w.XB, nb, Tb, K, z.nkbK, st));
-  AR_TRY_C(ar_launch_block_transpose(X, w.XTB, nb, Tb, K, z.nkbT, 2, st));
+  AR_TRY_C(ar_launch_stage_x(X, w.XTB, w.XB, nb, Tb, K, z.nkbT, z.nkbK, st));
   AR_TRY_C(ar_launch_block_transpose(Y, w.YB, nb, Tb, N, z.nkbT, (int)ysz, st));
   AR_TRY_C(ar_launch_fill_f32(reinterpret_cast<float*>(w.WB), 0.0f, z.wb / 2, st));
   // initial state: V = 0, the initial clip factors, best = initial, best loss = +inf

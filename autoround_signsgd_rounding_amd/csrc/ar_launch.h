@@ -72,6 +72,10 @@ ar_status ar_launch_block_copy(const uint16_t* src, uint16_t* dst, int64_t batch
 // batch of row-major [R, C] -> blocked (rows C, reduction R); elem_bytes 2 or 4
 ar_status ar_launch_block_transpose(const void* src, void* dst, int64_t batch, int64_t R,
                                     int64_t C, int64_t nkb, int elem_bytes, hipStream_t st);
+// X [batch][Tb, K] bf16 -> XTB (rows K, reduction Tb) and XB (rows Tb, reduction K),
+// both blocked, from one read of X.
+ar_status ar_launch_stage_x(const uint16_t* X, uint16_t* XTB, uint16_t* XB, int64_t batch,
+                            int64_t Tb, int64_t K, int64_t nkbT, int64_t nkbK, hipStream_t st);
 
 // Quantizer / update kernels (ar_quant.hip)
 // out_dt: dtype of Wq (AR_BF16 or AR_F32); alpha/beta NULL means the initial clip

@@ -272,12 +272,15 @@ __global__ __launch_bounds__(NT) void k_block_copy(const uint16_t* __restrict__ 
 // destination block (256 dst rows x 32 reduction elements, contiguous in dst):
 // the 32 x 256 source tile is read with 16-byte loads along its rows into LDS,
 // and the block is written out linearly, 16 bytes per lane, each chunk
-// gathered from a tile column.
+// gathered from a tile column. With rdst, the same tile also goes to the
+// untransposed blocked copy (rows R, reduction C, rnkb k-blocks): its 8
+// k-blocks of 32 rows, 2 KiB contiguous each, so src is read once for both.
 template <typename T>
 __global__ __launch_bounds__(NT) void k_block_transpose(const T* __restrict__ src, T* __restrict__ dst,
                                                         int64_t R, int64_t C, int64_t nkb,
                                                         int64_t src_batch, int64_t dst_batch,
-                                                        int vec) {
+                                                        int vec, T* __restrict__ rdst, int64_t rnkb,
+                                                        int64_t rdst_batch) {
   constexpr int EPC = 16 / (int)sizeof(T);            // elements per 16-byte piece
   constexpr int TS = arblk::ROWS + 16 / (int)sizeof(T); // tile row stride (elements)
   __shared__ __attribute__((aligned(16))) T tile[arblk::KB * TS];
@@ -300,6 +303,22 @@ __global__ __launch_bounds__(NT) void k_block_transpose(const T* __restrict__ sr
     *reinterpret_cast<u32x4_t*>(tile + rk * TS + pc * EPC) = *reinterpret_cast<const u32x4_t*>(v);
   }
   __syncthreads();
+  if (rdst != nullptr) {
+    // piece (j, rk, lc): k-block c0/32 + j, row r0 + rk, logical chunk lc (8 elements)
+    T* rd = rdst + b * rdst_batch;
+    for (int q = threadIdx.x; q < 8 * arblk::KB * 4; q += NT) {
+      const int j = q >> 7, rk = (q >> 2) & 31, lc = q & 3;
+      const int64_t k = c0 + 32 * j + 8 * lc;
+      if (k >= rnkb * arblk::KB) continue;
+      T v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = tile[rk * TS + 32 * j + 8 * lc + e];
+      T* d = rd + arblk::chunk_offset(r0 + rk, k, rnkb);
+#pragma unroll
+      for (int h = 0; h < 8 / EPC; ++h)
+        reinterpret_cast<u32x4_t*>(d)[h] = *reinterpret_cast<const u32x4_t*>(v + h * EPC);
+    }
+  }
   // chunk q of the block: dst row q / 4, stored chunk q % 4 = logical chunk ^ swizzle
   for (int q = threadIdx.x; q < arblk::ROWS * 4; q += NT) {
     const int rr = q >> 2, lc = (q & 3) ^ ((rr >> 2) & 3);
@@ -637,11 +656,28 @@ ar_status ar_launch_block_transpose(const void* src, void* dst, int64_t batch, i
   if (elem_bytes == 2)
     hipLaunchKernelGGL(k_block_transpose<uint16_t>, grid, dim3(NT), 0, st,
                        static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), R, C, nkb,
-                       R * C, dst_batch, vec);
+                       R * C, dst_batch, vec, (uint16_t*)nullptr, (int64_t)0, (int64_t)0);
   else
     hipLaunchKernelGGL(k_block_transpose<uint32_t>, grid, dim3(NT), 0, st,
                        static_cast<const uint32_t*>(src), static_cast<uint32_t*>(dst), R, C, nkb,
-                       R * C, dst_batch, vec);
+                       R * C, dst_batch, vec, (uint32_t*)nullptr, (int64_t)0, (int64_t)0);
+  return last_status();
+}
+
+ar_status ar_launch_stage_x(const uint16_t* X, uint16_t* XTB, uint16_t* XB, int64_t batch,
+                            int64_t Tb, int64_t K, int64_t nkbT, int64_t nkbK, hipStream_t st) {
+  if (batch <= 0 || Tb <= 0 || K <= 0) return AR_OK;
+  if (nkbT > 65535 || batch > 65535) return AR_ERR_SHAPE;   // grid y / z
+  // the transpose's blocks cover every XB row (nkbT·32 = row_tiles(Tb)·256) and k-block
+  if (nkbT * arblk::KB != arblk::row_tiles(Tb) * arblk::ROWS ||
+      nkbK > arblk::row_tiles(K) * (arblk::ROWS / arblk::KB))
+    return AR_ERR_SHAPE;
+  const int64_t xtb_batch = arblk::row_tiles(K) * nkbT * arblk::BLOCK_ELEMS;
+  const int64_t xb_batch = arblk::row_tiles(Tb) * nkbK * arblk::BLOCK_ELEMS;
+  const dim3 grid((unsigned)arblk::row_tiles(K), (unsigned)nkbT, (unsigned)batch);
+  const int vec = K % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
+  hipLaunchKernelGGL(k_block_transpose<uint16_t>, grid, dim3(NT), 0, st, X, XTB, Tb, K, nkbT,
+                     Tb * K, xtb_batch, vec, XB, nkbK, xb_batch);
   return last_status();
 }
 
