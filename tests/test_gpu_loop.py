@@ -75,17 +75,19 @@ def test_iters_zero_is_rtn():
     assert not out.V.any() and torch.all(out.alpha == 1.0)
 
 
-def test_loop_equals_repeated_steps():
+@pytest.mark.parametrize("K,gs", [(256, 64), (520, 40)])
+def test_loop_equals_repeated_steps(K, gs):
     """ar_tune_linear runs the same kernels as ar_tune_step: 7 steps over 3
-    minibatches give the bit-identical best state and loss sequence."""
-    N, K, seqlen, nsamples = 192, 256, 40, 3
+    minibatches give the bit-identical best state and loss sequence. K = 520
+    spans three 256-wide tiles of the staged input, the last one partial."""
+    N, seqlen, nsamples = 192, 40, 3
     case = synth.make_case(N, K, nsamples * seqlen, wdtype="bf16", seed=21)
     Yf, Yd = _targets(case)
-    cfg = ar.Config(bits=3, group_size=64, nsamples=nsamples, seqlen=seqlen, batch_samples=1,
+    cfg = ar.Config(bits=3, group_size=gs, nsamples=nsamples, seqlen=seqlen, batch_samples=1,
                     iters=7)
     Wd, Xd = weight_dev(case), bf16_dev(case.X_bits)
     out = ar.tune_linear(Wd, Xd, Yd, cfg)
-    G = K // 64
+    G = K // gs
     V = torch.zeros((N, K), device=dev())
     a = torch.ones((N, G), device=dev())
     b = torch.ones((N, G), device=dev())
