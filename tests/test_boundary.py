@@ -176,6 +176,50 @@ def test_tune_linear_validation():
     assert run(codes=NULL) == INV
     assert run(W=NULL) == INV
     assert run(cref=cfg(bits=7)[0]) == UNSUP
+    assert run(codes=ctypes.c_void_p(0x100004)) == INV                  # codes 8-byte aligned
+    assert run(cref=cfg(nsamples=3, seqlen=64, batch_samples=2, iters=3)[0]) == SHAPE
+    assert run(cref=cfg(nsamples=2, seqlen=64, batch_samples=1, group_size=48)[0]) == SHAPE
+    assert run(cref=cfg(nsamples=2, seqlen=64, batch_samples=1, group_size=12)[0]) == UNSUP
+    assert ar.lib.ar_tune_linear(c, 1, P, 8, 128, P_MIS, P, 1, P, P, P, NULL, NULL, NULL, NULL,
+                                 NULL, P, need, None, NULL) == INV      # X misaligned
+
+
+def test_gram_validation():
+    """The Gram-form entry points check their arguments as the token form does."""
+    c, _ = cfg(nsamples=2, seqlen=64, batch_samples=1, iters=3)
+    n = ctypes.c_size_t()
+    assert ar.lib.ar_gram_workspace_size(c, 1, 8, 128, 1, ctypes.byref(n)) == OK
+    need = n.value
+    assert need > 0
+    assert ar.lib.ar_gram_workspace_size(c, 1, 8, 128, 1, None) == INV
+    assert ar.lib.ar_gram_workspace_size(c, 5, 8, 128, 1, ctypes.byref(n)) == UNSUP
+    assert ar.lib.ar_gram_workspace_size(cfg(nsamples=3, seqlen=64, batch_samples=2)[0], 1, 8,
+                                         128, 1, ctypes.byref(n)) == SHAPE
+    sn = ctypes.c_size_t()
+    assert ar.lib.ar_gram_step_workspace_size(c, 1, 8, 128, 64, 1, ctypes.byref(sn)) == OK
+    assert ar.lib.ar_gram_step_workspace_size(c, 1, 8, 128, 60, 1, ctypes.byref(sn)) == SHAPE
+    assert ar.lib.ar_gram_step_workspace_size(c, 1, 8, 128, 64, 7, ctypes.byref(sn)) == UNSUP
+
+    def step(st, Tb=64, loss=P, ws_bytes=None, Xb=P):
+        nb = sn.value if ws_bytes is None else ws_bytes
+        return ar.lib.ar_tune_step_gram(c, ctypes.byref(st), Xb, P, 1, Tb, loss, NULL, NULL,
+                                        NULL, 1, P, nb, NULL)
+    assert step(_state(), ws_bytes=sn.value - 1) == WS
+    assert step(_state(best_V=0x500000)) == INV
+    assert step(_state(), loss=NULL) == INV
+    assert step(_state(), Xb=P_MIS) == INV
+    assert step(_state(), Tb=60) == SHAPE
+    assert step(_state(wdt=3)) == UNSUP
+    assert ar.lib.ar_tune_step_gram(c, None, P, P, 1, 64, P, NULL, NULL, NULL, 1, P, sn.value,
+                                    NULL) == INV
+
+    def run(codes=P, ws_bytes=need, X=P, cref=c):
+        return ar.lib.ar_tune_linear_gram(cref, 1, P, 8, 128, X, P, 1, codes, P, P, NULL, NULL,
+                                          NULL, NULL, NULL, P, ws_bytes, None, NULL)
+    assert run(ws_bytes=need - 1) == WS
+    assert run(codes=NULL) == INV
+    assert run(X=P_MIS) == INV
+    assert run(cref=cfg(bits=7, nsamples=2, seqlen=64, batch_samples=1)[0]) == UNSUP
 
 
 def test_pack_validation():
