@@ -1,0 +1,91 @@
+"""Planted mistakes in the CPU oracle, for test_oracle_mutants.py.
+
+Each entry names one oracle function and a one-place edit of its source text
+that a plausible slip would produce: a dropped term, a wrong sign, an
+off-by-one, another rounding mode, a wrong index or a transposed operand. The
+edit must match the source exactly once, so a change to the oracle that moves
+the target makes the test fail loudly rather than test nothing. ``apply``
+compiles the edited function into the oracle module's namespace (every other
+oracle function then calls the planted version) and rebinds the package-level
+name. Nothing is written to disk; only a pytest process started with
+AR_ORACLE_MUTANT set loads this (through conftest.py).
+"""
+import inspect
+
+MUTANTS = {
+    # bf16 rounding: truncation instead of round-to-nearest-even
+    "bf16_truncate": ("bf16", "upper = upper + up.astype(np.uint32)", "upper = upper"),
+    # group min/max over strided instead of contiguous channels
+    "strided_groups": ("group_minmax",
+                       "Wg = np.asarray(W, dtype=F32).reshape(N, K // g, g)",
+                       "Wg = np.asarray(W, dtype=F32).reshape(N, g, K // g).transpose(0, 2, 1)"),
+    # scale and zero-point
+    "zp_sign": ("qparams", "np.rint(-lo / s)", "np.rint(lo / s)"),
+    "scale_off_by_one": ("qparams", "s = (hi - lo) / maxq", "s = (hi - lo) / (maxq + F32(1.0))"),
+    "range_not_anchored_at_zero": ("qparams", "lo = np.minimum(alpha * wmin, F32(0.0))",
+                                   "lo = alpha * wmin"),
+    "sym_scale_halved": ("qparams", "s = (F32(2.0) * amax) / maxq", "s = amax / maxq"),
+    "sym_zero_point": ("qparams", "F32(2 ** (bits - 1))", "F32(2 ** (bits - 1) - 1)"),
+    # fake-quantization
+    "round_half_up": ("fake_quant", "r = np.rint(u)", "r = np.floor(u + F32(0.5))"),
+    "offset_after_rounding": ("fake_quant", "    u = t + V\n    r = np.rint(u)\n",
+                              "    u = t\n    r = np.rint(u) + V\n"),
+    "mask_from_clamped_code": ("fake_quant", "m = (c >= 0) & (c <= maxq)",
+                               "m = (q >= 0) & (q <= maxq)"),
+    "dequant_drops_zero_point": ("fake_quant", "what = s_e * (q - zp_e)", "what = s_e * q"),
+    # loss and weight gradient
+    "grad_factor_half": ("forward_backward", "G = (2.0 / (T * Nn))", "G = (1.0 / (T * Nn))"),
+    "loss_mean_over_tokens_only": ("forward_backward",
+                                   "return loss_sum / (T * Nn), G, loss_sum",
+                                   "return loss_sum / T, G, loss_sum"),
+    "residual_sign": ("forward_backward", "R = Yp - np.asarray(Yb, F64)",
+                      "R = np.asarray(Yb, F64) - Yp"),
+    "grad_transposed": ("forward_backward", "(dY.T @ X64)", "(X64.T @ dY)"),
+    # straight-through gradients
+    "ste_no_mask": ("ste_grads", "gV = G64 * fq.s_e.astype(F64) * m", "gV = G64 * fq.s_e.astype(F64)"),
+    "ste_scale_term_drops_t": ("ste_grads", "(qz - m * fq.t.astype(F64))", "qz"),
+    "ste_zero_point_sign": ("ste_grads", "B = -s64 * Bsum", "B = s64 * Bsum"),
+    "ste_dlo_drops_zp_term": ("ste_grads", "dlo = -D / maxq - B / s64", "dlo = -D / maxq"),
+    "ste_sym_routed_wrong": ("ste_grads", "        ga = np.where(to_alpha, damax",
+                             "        to_alpha = ~to_alpha\n        ga = np.where(to_alpha, damax"),
+    # SignSGD
+    "sgn_of_zero_is_one": ("sgn", "(x > 0).astype(F32)", "(x >= 0).astype(F32)"),
+    "offset_clamp_too_wide": ("signsgd_update", "F32(-0.5), F32(0.5)", "F32(-1.0), F32(1.0)"),
+    "minmax_lr_ignored": ("signsgd_update", "mlr = F32(cfg.mlr)", "mlr = F32(cfg.lr)"),
+    "offset_step_ascends": ("signsgd_update", "np.asarray(V, F32) - lr * sgn(gV)",
+                            "np.asarray(V, F32) + lr * sgn(gV)"),
+    # the loop's best-loss snapshot
+    "snapshot_after_update": ("tune_linear", "            best = (V.copy(), alpha.copy(), beta.copy())",
+                              "            best = (r.V.copy(), r.alpha.copy(), r.beta.copy())"),
+    "snapshot_on_ties": ("tune_linear", "if r.loss < best_loss:", "if r.loss <= best_loss:"),
+    "last_state_kept": ("tune_linear", "        V, alpha, beta = best\n", "        pass\n"),
+    "one_minibatch_only": ("tune_linear", "Xb, Yb = minibatch(i % nb)", "Xb, Yb = minibatch(0)"),
+    # Gram form
+    "gram_cross_term_sign": ("forward_backward_gram", "2.0 * np.sum(D * st.Cn)",
+                             "-2.0 * np.sum(D * st.Cn)"),
+    "gram_drops_e2": ("forward_backward_gram", " + st.e2)", ")"),
+    # MSE initial scale
+    "mse_grid_skips_one": ("mse_grid_points", "p = F32(1.0 - j / cfg.mse_grid)",
+                           "p = F32(1.0 - (j + 1) / cfg.mse_grid)"),
+    "mse_picks_largest_error": ("mse_shrink", "best = np.argmin(np.stack(errs), axis=0)",
+                                "best = np.argmax(np.stack(errs), axis=0)"),
+    # packing
+    "pack_drops_straddling_bits": ("_pack_axis0",
+                                   "            out[w + 1] |= v[k] >> np.uint64(32 - off)\n",
+                                   "            pass\n"),
+    "pack_field_order_reversed": ("_pack_axis0", "out[w] |= (v[k] << np.uint64(off))",
+                                  "out[w] |= (v[L - 1 - k] << np.uint64(off))"),
+}
+
+
+def apply(name: str) -> None:
+    import oracle
+    import oracle.autoround_ref as R
+    fn, old, new = MUTANTS[name]
+    src = inspect.getsource(getattr(R, fn))
+    n = src.count(old)
+    if n != 1:
+        raise RuntimeError(f"mutant {name}: target occurs {n} times in {fn}")
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), R.__dict__)
+    if hasattr(oracle, fn):
+        setattr(oracle, fn, R.__dict__[fn])

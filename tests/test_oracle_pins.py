@@ -357,6 +357,31 @@ def test_best_snapshot_not_worse_than_rtn():
         assert r.alpha.min() >= 0.5 and r.beta.max() <= 1.0
 
 
+def test_snapshot_keeps_the_first_of_equal_losses():
+    """The snapshot takes a state only when its loss is strictly below every
+    earlier one (llm-compressor AutoRound page, the tuning loop's best-loss
+    bookkeeping). With both step sizes zero the state never moves, every step
+    has the same loss, and the first step stays the best."""
+    W, X, Y = _full_batch_problem()
+    cfg = _cfg(bits=4, group_size=16, iters=6, lr=0.0, minmax_lr=0.0)
+    r = O.tune_linear(W, lambda b: (X, Y), 1, cfg)
+    assert len(set(r.losses)) == 1
+    assert r.best_step == 0 and r.best_loss == r.losses[0]
+
+
+def test_steps_cycle_through_minibatches():
+    """Step i draws minibatch i mod nb (the tuning loop walks the calibration
+    batches in turn); the same three minibatches are requested in order."""
+    W, X, Y = _full_batch_problem()
+    seen = []
+
+    def minibatch(b):
+        seen.append(b)
+        return X, Y
+    O.tune_linear(W, minibatch, 3, _cfg(bits=4, group_size=16, iters=8))
+    assert seen == [0, 1, 2, 0, 1, 2, 0, 1]
+
+
 def test_brute_force_2x4():
     """2x4 weight, 2-bit asym, one group per row, s and zp frozen
     (minmax_lr = 0), exact arithmetic: neither RTN nor 200 SignSGD steps can
