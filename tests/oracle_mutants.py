@@ -7,7 +7,7 @@ edit must match the source exactly once, so a change to the oracle that moves
 the target makes the test fail loudly rather than test nothing. ``apply``
 compiles the edited function into the oracle module's namespace (every other
 oracle function then calls the planted version) and rebinds the package-level
-name. Nothing is written to disk; only a pytest process started with
+name where the package re-exports it. Nothing is written to disk; only a pytest process started with
 AR_ORACLE_MUTANT set loads this (through conftest.py).
 """
 import inspect
@@ -75,17 +75,48 @@ MUTANTS = {
                                    "            pass\n"),
     "pack_field_order_reversed": ("_pack_axis0", "out[w] |= (v[k] << np.uint64(off))",
                                   "out[w] |= (v[L - 1 - k] << np.uint64(off))"),
+    # block forward (oracle/block_ref.py)
+    "rmsnorm_sum_not_mean": ("block_ref.rmsnorm", "np.mean(x.astype(F64) ** 2", "np.sum(x.astype(F64) ** 2"),
+    "rmsnorm_weight_dropped": ("block_ref.rmsnorm", " * np.asarray(w, F32))", ")"),
+    "rope_rotation_sign": ("block_ref.rope", "(a * c).astype(F32) - (b * s).astype(F32)",
+                           "(a * c).astype(F32) + (b * s).astype(F32)"),
+    "rope_global_positions": ("block_ref.rope", "pos = np.arange(M) % seqlen", "pos = np.arange(M)"),
+    "rope_frequency_exponent": ("block_ref.rope_table", "inv = theta ** (-2.0 * j / Dh)",
+                                "inv = theta ** (-1.0 * j / Dh)"),
+    "attention_not_causal": ("block_ref.attention", "S[mask] = -np.inf", "pass"),
+    "attention_scale": ("block_ref.attention", "/ np.sqrt(Dh)", "/ Dh"),
+    "attention_keys_of_first_sequence": ("block_ref.attention", "k[s0:s0 + seqlen, sl].T",
+                                         "k[0:seqlen, sl].T"),
+    "silu_sign": ("block_ref.silu_mul", "np.exp(-g)", "np.exp(g)"),
+    "attention_residual_dropped": ("block_ref.block_forward", 't["h1"] = add(t["h"], t["o_proj"])',
+                                   't["h1"] = t["o_proj"]'),
+    "mlp_norm_of_block_input": ("block_ref.block_forward", 't["m"] = rmsnorm(t["h1"], norms[1]',
+                                't["m"] = rmsnorm(t["h"], norms[1]'),
+    "tuning_ignores_quantized_inputs": ("block_ref.tune_block",
+                                        "X = q[LINEAR_INPUT[name]] if quanted_input else fp[LINEAR_INPUT[name]]",
+                                        "X = fp[LINEAR_INPUT[name]]"),
+    "tuning_targets_quantized_pipeline": ("block_ref.tune_block", "Y = fp[name]", "Y = q[name]"),
+    "tuned_linear_not_substituted": ("block_ref.tune_block", "Wq[name] = b16(res.what)", "pass"),
 }
+
+
+def target(name: str):
+    """(module, function name) of a mutant: "block_ref.f" lives in
+    oracle/block_ref.py, a bare name in oracle/autoround_ref.py."""
+    import importlib
+    fn = MUTANTS[name][0]
+    mod, _, fname = fn.rpartition(".")
+    return importlib.import_module("oracle." + (mod or "autoround_ref")), fname
 
 
 def apply(name: str) -> None:
     import oracle
-    import oracle.autoround_ref as R
     fn, old, new = MUTANTS[name]
-    src = inspect.getsource(getattr(R, fn))
+    mod, fname = target(name)
+    src = inspect.getsource(getattr(mod, fname))
     n = src.count(old)
     if n != 1:
         raise RuntimeError(f"mutant {name}: target occurs {n} times in {fn}")
-    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), R.__dict__)
-    if hasattr(oracle, fn):
-        setattr(oracle, fn, R.__dict__[fn])
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    if mod.__name__ == "oracle.autoround_ref" and hasattr(oracle, fname):
+        setattr(oracle, fname, mod.__dict__[fname])

@@ -72,6 +72,49 @@ def test_rmsnorm_scale_invariance_and_unit_rows():
     np.testing.assert_array_equal(B.rmsnorm(ones, np.ones(32, F32), 0.0), ones)
 
 
+def test_rmsnorm_applies_the_weight_per_channel():
+    """Power-of-two channel weights scale each output column exactly (the
+    products and the bf16 rounding commute with them)."""
+    rng = np.random.default_rng(5)
+    x = B.b16(rng.standard_normal((6, 32)).astype(F32))
+    w = (2.0 ** (np.arange(32) % 5 - 2)).astype(F32)
+    base = B.rmsnorm(x, np.ones(32, F32), 1e-6)
+    np.testing.assert_array_equal(B.rmsnorm(x, w, 1e-6), base * w)
+
+
+def test_rope_rotates_by_the_closed_form_angles():
+    """A head vector with ones in its first half and zeros in its second half
+    turns, pair j at position p, into (cos a, sin a) with a = p·theta^(−2j/Dh)."""
+    S, H, Dh, theta = 12, 1, 8, 10000.0
+    x = np.zeros((S, Dh), F32)
+    x[:, :Dh // 2] = 1.0
+    y = B.rope(x, S, H, theta)
+    for p in range(S):
+        for j in range(Dh // 2):
+            a = p * theta ** (-2.0 * j / Dh)
+            assert abs(y[p, j] - np.cos(a)) <= 4e-3 and abs(y[p, Dh // 2 + j] - np.sin(a)) <= 4e-3
+
+
+def test_silu_values():
+    """SiLU(g)·u against g/(1 + e^−g) at a few points."""
+    g = np.array([[0.0, 1.0, -1.0, 4.0, -4.0, 0.5]], F32)
+    u = np.array([[1.0, 1.0, 1.0, 1.0, 2.0, -3.0]], F32)
+    want = [float(a) / (1.0 + np.exp(-float(a))) * float(b) for a, b in zip(g[0], u[0])]
+    np.testing.assert_allclose(B.silu_mul(g, u)[0], want, rtol=2 ** -8, atol=1e-7)
+
+
+def test_mlp_sees_the_attention_output():
+    """The MLP normalises the residual stream after attention: with the
+    attention output projection zeroed it sees RMSNorm(h), and any other
+    output projection changes what it sees."""
+    dims, W, norms, h = _toy(1)
+    Z = dict(W, o_proj=np.zeros_like(W["o_proj"]))
+    t0 = B.block_forward(h, Z, norms, dims)
+    np.testing.assert_array_equal(t0["m"], B.rmsnorm(h, norms[1], dims.rms_eps))
+    t1 = B.block_forward(h, W, norms, dims)
+    assert not np.array_equal(t1["m"], t0["m"])
+
+
 def _toy(nsamples=4):
     dims = synth.BLOCKS["toy_block"]
     c = synth.make_block_case(dims, nsamples=nsamples)

@@ -1,6 +1,7 @@
 """The oracle's pins are strong enough to catch plausible mistakes: with each
 planted mistake of oracle_mutants.py compiled into the oracle (in a child
-pytest process), at least one pin of test_oracle_pins.py must fail."""
+pytest process), at least one pin of test_oracle_pins.py or
+test_block_oracle.py must fail."""
 import os
 import subprocess
 import sys
@@ -8,15 +9,15 @@ from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
-from oracle_mutants import MUTANTS, apply
+from oracle_mutants import MUTANTS, apply, target
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-PINS = os.path.join(HERE, "test_oracle_pins.py")
+PINS = [os.path.join(HERE, "test_oracle_pins.py"), os.path.join(HERE, "test_block_oracle.py")]
 
 
 def _run_pins(mutant):
     env = dict(os.environ, AR_ORACLE_MUTANT=mutant)
-    r = subprocess.run([sys.executable, "-m", "pytest", PINS, "-x", "-q", "-p", "no:cacheprovider",
+    r = subprocess.run([sys.executable, "-m", "pytest", *PINS, "-x", "-q", "-p", "no:cacheprovider",
                         "-m", "not gpu"], cwd=os.path.dirname(HERE), env=env,
                        capture_output=True, text=True, timeout=600)
     return mutant, r.returncode, r.stdout[-2000:]
@@ -26,17 +27,16 @@ def _run_pins(mutant):
 def test_mutant_applies(name):
     """Every edit still matches the oracle's source exactly once and compiles."""
     import oracle
-    import oracle.autoround_ref as R
-    fn = MUTANTS[name][0]
-    orig = R.__dict__[fn]
-    orig_pkg = getattr(oracle, fn, None)
+    mod, fname = target(name)
+    orig = mod.__dict__[fname]
+    orig_pkg = getattr(oracle, fname, None)
     try:
         apply(name)
-        assert R.__dict__[fn] is not orig
+        assert mod.__dict__[fname] is not orig
     finally:
-        R.__dict__[fn] = orig
+        mod.__dict__[fname] = orig
         if orig_pkg is not None:
-            setattr(oracle, fn, orig_pkg)
+            setattr(oracle, fname, orig_pkg)
 
 
 def test_every_mutant_fails_a_pin():
