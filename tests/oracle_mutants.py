@@ -75,6 +75,32 @@ MUTANTS = {
                                    "            pass\n"),
     "pack_field_order_reversed": ("_pack_axis0", "out[w] |= (v[k] << np.uint64(off))",
                                   "out[w] |= (v[L - 1 - k] << np.uint64(off))"),
+    "unpack_drops_straddling_bits": ("_unpack_axis0",
+                                     "            val |= w64[w + 1] << np.uint64(32 - off)\n",
+                                     "            pass\n"),
+    # packed-format dequantization and product
+    "dequant_sym_zero_point": ("dequantize", "zp = np.full((N, K // g), 2 ** (bits - 1), np.int64)",
+                               "zp = np.full((N, K // g), 2 ** (bits - 1) - 1, np.int64)"),
+    "dequant_ignores_zero_points": ("dequantize", "(codes.astype(F32) - zp_e)", "codes.astype(F32)"),
+    "dequant_product_not_bf16": ("dequant_matmul", "bf16(what).astype(F64).T", "what.astype(F64).T"),
+    # Gram statistics and initial clip factors
+    "gram_residual_sign": ("gram_stats", "E = X64 @ np.asarray(W, F64).T - np.asarray(Yb, F64)",
+                           "E = np.asarray(Yb, F64) - X64 @ np.asarray(W, F64).T"),
+    "init_clip_ignores_shrink": ("init_clip", "a = np.full((N, Gn), F32(cfg.minmax_shrink), F32)",
+                                 "a = np.full((N, Gn), F32(1.0), F32)"),
+    # per-layer configuration
+    "layer_pattern_prefix_match": ("resolve_layer_config", "if re.fullmatch(key, name):",
+                                   "if re.match(key, name):"),
+    "layer_exact_key_defaults_outside_set": ("resolve_layer_config",
+                                             'cfg.get("bits", bits if quantized else 16)',
+                                             'cfg.get("bits", bits)'),
+    "layer_plain_keys_as_patterns": ("resolve_layer_config",
+                                     "        if not any(c in REGEX_SPECIAL_CHARS for c in key):\n"
+                                     "            continue\n", ""),
+    "fused_configs_not_compared": ("resolve_fused_config", "if len(set(cfgs)) != 1:", "if False:"),
+    "fused_experts_not_collected": ("resolve_fused_config",
+                                    "names = [k for k, _ in rules if k.startswith(layer_name)]",
+                                    "names = []"),
     # block forward (oracle/block_ref.py)
     "rmsnorm_sum_not_mean": ("block_ref.rmsnorm", "np.mean(x.astype(F64) ** 2", "np.sum(x.astype(F64) ** 2"),
     "rmsnorm_weight_dropped": ("block_ref.rmsnorm", " * np.asarray(w, F32))", ")"),

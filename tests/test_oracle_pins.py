@@ -470,6 +470,22 @@ def _mse_err(W, p, cfg):
     return (d * d).reshape(N, K // g, g).sum(axis=2)
 
 
+def test_minmax_shrink_sets_the_initial_clip_factors():
+    """With the Min-Max initial scale, alpha = beta = minmax_shrink in every
+    group (llm-compressor AutoRound page, constructor parameter table), so a
+    group whose range straddles zero gets 0.8 times the unshrunk scale."""
+    rng = np.random.default_rng(7)
+    W = rng.standard_normal((4, 32)).astype(F32)
+    cfg = _cfg(bits=4, group_size=16, minmax_shrink=0.8, clip_lo=0.5)
+    a, b = O.init_clip(W, cfg)
+    assert a.shape == (4, 2) and np.all(a == F32(0.8)) and np.all(b == F32(0.8))
+    wmin, wmax = O.group_minmax(W, 16)
+    assert np.all(wmin < 0) and np.all(wmax > 0)
+    s08 = O.rtn_quant(W, cfg)[1]
+    s10 = O.rtn_quant(W, _cfg(bits=4, group_size=16))[1]
+    np.testing.assert_allclose(s08, 0.8 * s10, rtol=1e-6)
+
+
 def test_mse_grid_points():
     pts = O.mse_grid_points(O.Config())
     assert len(pts) == 51 and pts[0] == 1.0 and pts[-1] == F32(0.5)
@@ -568,6 +584,13 @@ def test_layer_config_exact_then_regex():
     assert O.resolve_layer_config(rules, DEF, True, "model.layers.2.self_attn.o_proj") == DEF
 
 
+def test_layer_config_patterns_match_whole_names():
+    """A pattern must match the whole layer name, not a prefix of it."""
+    rules = [(r"model\.layers\.2", {"bits": 4, "sym": True})]
+    assert O.resolve_layer_config(rules, DEF, True, "model.layers.2.self_attn.o_proj") == DEF
+    assert O.resolve_layer_config(rules, DEF, True, "model.layers.2") == (4, 128, True)
+
+
 def test_layer_config_plain_keys_are_not_patterns():
     """'.' is not in the special set: a dotted key is only an exact name."""
     rules = [("model.layers.0.mlp", {"bits": 8})]
@@ -635,6 +658,22 @@ def test_dequant_matmul_hand_example():
     Y = O.dequant_matmul(X, qw, qz, scale, 4, 8, 8, 8)
     np.testing.assert_allclose(Y[0, :2], [2.5, 1.75])
     assert not Y[0, 2:].any()
+
+
+def test_dequant_product_uses_the_bf16_weight():
+    """The product's weight operand is bf16(Ŵ), the operand of the tuning
+    loop's forward product: scale float32(0.1), code 3, zero-point 0 give
+    Ŵ = 0.3000000119 in float32, whose bf16 value is 0.30078125 (0x3E9A)."""
+    codes = np.zeros((8, 8), np.uint8)
+    codes[0, 0] = 3
+    zp = np.zeros((8, 1), np.uint8)
+    scale = np.zeros((8, 1), F32)
+    scale[0, 0] = F32(0.1)
+    qw, qz = O.pack(codes, zp, 4)
+    X = np.zeros((1, 8), F32)
+    X[0, 0] = 1.0
+    Y = O.dequant_matmul(X, qw, qz, scale, 4, 8, 8, 8)
+    assert Y[0, 0] == 0.30078125
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
