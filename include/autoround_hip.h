@@ -179,8 +179,9 @@ ar_status ar_tune_step(const ar_config* cfg, const ar_state* state, const uint16
    Wq [N, K] wdt (nullable); V_out [N, K], alpha_out/beta_out [N, G] float32 final
    (restored) state (nullable); losses [iters] float32 per-step loss (nullable).
    ws: ar_workspace_size bytes. times: when non-NULL, per-kernel device times of
-   every times->sample_every-th step are measured with HIP events and the call
-   blocks until the stream has drained. */
+   every times->sample_every-th step are measured with HIP events and, with
+   iters > 0, the call blocks until the stream has drained (iters = 0 leaves the
+   times at zero and does not block). */
 ar_status ar_tune_linear(const ar_config* cfg, int32_t wdt, const void* W, int64_t N, int64_t K,
                          const uint16_t* X, const void* Y, int32_t ydt, uint8_t* codes,
                          float* scale, uint8_t* zp, void* Wq, float* V_out, float* alpha_out,
