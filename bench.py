@@ -102,7 +102,28 @@ def _cpu_baseline(case, Yd, w, steps=8):
                       f"full {w.N}x{w.K} problem on {Tb}-token minibatches; "
                       f"{el / steps:.2f} s/step; a 200-iteration run extrapolates to "
                       f"{200 * el / steps / 60:.1f} min",
-            "host_cpus": os.cpu_count(), "host": platform.processor() or platform.machine()}
+            "host_cpus": os.cpu_count(), "affinity_cpus": _affinity(),
+            "blas_threads": int(threads), "cpu_model": _cpu_model(),
+            "host": platform.processor() or platform.machine()}
+
+
+def _affinity():
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        return None
+
+
+def _cpu_model():
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return platform.processor() or None
 
 
 def _dequant_run(ar, torch, X, out, w, reps=20):
