@@ -21,6 +21,7 @@ RULES = [
     (r"model\.layers\.[0-9]{2}\..*", {"group_size": -1}),
     ("m.q_proj", {"bits": 8}), ("m.k_proj", {"bits": 8}), ("m.v_proj", {"bits": 4}),
     ("e.experts.0.w1", {"bits": 3}), ("e.experts.1.w1", {"bits": 3}),
+    (r"model\.layers\.4", {"bits": 2}),                 # matches a prefix of longer names only
 ]
 NAMES = [
     "model.layers.0.mlp.down_proj", "model.layers.0.mlp.up_proj", "model.layers.1.mlp.gate_proj",
@@ -28,6 +29,7 @@ NAMES = [
     "model.layers.3.self_attn.k_proj", "model.layers.12.self_attn.o_proj",
     "x.model.layers.1.self_attn.q_proj", "model.layers.0.mlp", "modelXlayersX0Xmlp", "lm_head",
     "embed_tokens", "norm", "layers.(", "layers.7", "m.q_proj", "e.experts.0.w1",
+    "model.layers.4.self_attn.o_proj", "model.layers.4",
 ]
 
 
