@@ -1,5 +1,5 @@
 // Sequential block-wise tuning with quantized inputs (gfx950): the forward of a
-// Llama-style decoder block and the driver that tunes its seven Linears in
+// Llama-style decoder block and the host routine that tunes its seven Linears in
 // order, each on its input in the quantized pipeline (the block with the
 // Linears tuned so far) and its full-precision target (llm-compressor AutoRound
 // page: the per-subgraph loop; enable_quanted_input uses the previous layers'
