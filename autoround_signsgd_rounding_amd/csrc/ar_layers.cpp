@@ -13,6 +13,8 @@
 // Patterns use the ECMAScript grammar of std::regex; the pages' Python `re`
 // agrees with it on the constructs layer-name patterns use (literals, '.',
 // escapes, classes, groups, alternation, repetition, anchors).
+#include <algorithm>
+#include <cstring>
 #include <regex>
 #include <string>
 
@@ -20,12 +22,17 @@
 
 namespace {
 
-bool has_special(const char* key) {
-  static const char* kSpecial = "*+?^$()[]{}|\\";
-  for (const char* p = key; *p; ++p)
-    for (const char* q = kSpecial; *q; ++q)
-      if (*p == *q) return true;
-  return false;
+// A key is a pattern when it holds a regular-expression special character.
+bool has_special(const char* key) { return std::strpbrk(key, "*+?^$()[]{}|\\") != nullptr; }
+
+// True when key is a pattern that compiles and matches all of name.
+bool whole_name_match(const char* key, const char* name) {
+  if (!has_special(key)) return false;
+  try {
+    return std::regex_match(name, std::regex(key, std::regex::ECMAScript));
+  } catch (const std::regex_error&) {
+    return false;
+  }
 }
 
 ar_layer_qconfig unquantized() {
@@ -47,19 +54,13 @@ ar_layer_qconfig fill(const ar_layer_rule& r, const ar_layer_qconfig& base) {
 ar_layer_qconfig resolve(const ar_layer_rule* rules, int32_t n, const ar_layer_qconfig& d,
                          bool quantized, const char* name) {
   const ar_layer_qconfig fallback = quantized ? d : unquantized();
-  if (n == 0) return fallback;
-  for (int32_t i = 0; i < n; ++i)
-    if (std::string(rules[i].key) == name) return fill(rules[i], fallback);
-  for (int32_t i = 0; i < n; ++i) {
-    if (!has_special(rules[i].key)) continue;
-    try {
-      const std::regex re(rules[i].key, std::regex::ECMAScript);
-      if (std::regex_match(name, re)) return fill(rules[i], d);
-    } catch (const std::regex_error&) {
-      continue;
-    }
-  }
-  return fallback;
+  const ar_layer_rule* end = rules + n;
+  const ar_layer_rule* exact = std::find_if(
+      rules, end, [&](const ar_layer_rule& r) { return std::strcmp(r.key, name) == 0; });
+  if (exact != end) return fill(*exact, fallback);
+  const ar_layer_rule* pattern = std::find_if(
+      rules, end, [&](const ar_layer_rule& r) { return whole_name_match(r.key, name); });
+  return pattern != end ? fill(*pattern, d) : fallback;
 }
 
 bool same(const ar_layer_qconfig& a, const ar_layer_qconfig& b) {

@@ -586,56 +586,68 @@ def brute_force_rounding(W, X, Y, qp: QParams, bits: int, group_size: int):
 
 
 # ------------------------------------------------------------------ per-layer config
-REGEX_SPECIAL_CHARS = set("*+?^$()[]{}|\\")
+# A rule key is a pattern when it holds one of these characters; the set has
+# to be the same for every implementation, since it decides which keys match.
+REGEX_SPECIAL_CHARS = frozenset("*+?^$()[]{}|\\")
+_FIELDS = ("bits", "group_size", "sym")
+_UNQUANTIZED = (16, -1, True)       # "leave the layer unquantized"
+
+
+def _merge(rule_cfg: dict, fallback) -> tuple:
+    """(bits, group_size, sym): the rule's value where it sets one, else the
+    fallback's."""
+    return tuple(rule_cfg[f] if f in rule_cfg else fb for f, fb in zip(_FIELDS, fallback))
+
+
+def _whole_name_match(key: str, name: str) -> bool:
+    """True when ``key`` is a pattern that compiles and matches all of ``name``."""
+    if REGEX_SPECIAL_CHARS.isdisjoint(key):
+        return False
+    try:
+        return re.compile(key).fullmatch(name) is not None
+    except re.error:
+        return False
 
 
 def resolve_layer_config(rules, defaults, quantized: bool, name: str):
     """(bits, group_size, sym) of one layer from per-layer rules ([SGL]
     "2. 레이어별 개별 설정" and "3. 정규식 기반 레이어 매칭"). ``rules`` is an
     ordered list of (key, cfg dict with optional "bits", "group_size", "sym").
-      - no rules: the defaults, or (16, -1, True) for a layer outside the
-        quantized set;
-      - an exact key match: its values, the missing ones from the defaults
-        (from (16, -1, True) outside the quantized set);
-      - else the first key that contains a regular-expression special
-        character and fully matches the name: its values, missing ones from the
-        defaults; keys that do not compile are skipped;
-      - else as with no rules.
-    16 bits means "leave unquantized"."""
-    bits, gs, sym = defaults
-    unq = (16, -1, True)
+    The fallback is the defaults, or (16, -1, True) for a layer outside the
+    quantized set (16 bits: leave it unquantized).
+      - no rules: the fallback;
+      - a key equal to the name (the first such rule): its values, the
+        missing ones from the fallback;
+      - else the first key that is a pattern (holds a regular-expression
+        special character) and matches the whole name: its values, the
+        missing ones from the defaults; keys that do not compile never match;
+      - else the fallback."""
+    fallback = tuple(defaults) if quantized else _UNQUANTIZED
     if not rules:
-        return tuple(defaults) if quantized else unq
+        return fallback
+    by_key = {}
     for key, cfg in rules:
-        if key == name:
-            return (cfg.get("bits", bits if quantized else 16),
-                    cfg.get("group_size", gs if quantized else -1),
-                    cfg.get("sym", sym if quantized else True))
-    for key, cfg in rules:
-        if not any(c in REGEX_SPECIAL_CHARS for c in key):
-            continue
-        try:
-            if re.fullmatch(key, name):
-                return (cfg.get("bits", bits), cfg.get("group_size", gs), cfg.get("sym", sym))
-        except re.error:
-            continue
-    return tuple(defaults) if quantized else unq
+        by_key.setdefault(key, cfg)
+    if name in by_key:
+        return _merge(by_key[name], fallback)
+    hit = next((cfg for key, cfg in rules if _whole_name_match(key, name)), None)
+    return fallback if hit is None else _merge(hit, tuple(defaults))
 
 
 def resolve_fused_config(rules, defaults, quantized: bool, layer_name: str, sub_names=None):
     """Config of a fused layer ([SGL] "4. FusedMoE와 Fused QKV 처리"): all of its
-    sub-layers must resolve to the same config, else ValueError. With
-    ``sub_names`` (a fused q/k/v-style layer) those names are resolved; without
-    (a fused expert layer) the sub-layers are the rule keys that start with the
-    layer's name, and a layer with no such key resolves as itself."""
-    if sub_names is None:
-        names = [k for k, _ in rules if k.startswith(layer_name)]
-        if not names:
-            return resolve_layer_config(rules, defaults, quantized, layer_name)
+    sub-layers must resolve to one config, else ValueError. With ``sub_names``
+    (a fused q/k/v-style layer) those names are the sub-layers; without (a
+    fused expert layer) they are the rule keys that start with the layer's
+    name, and a layer with no such key resolves as itself."""
+    if sub_names is not None:
+        members = list(sub_names)
     else:
-        names = list(sub_names)
-    cfgs = [resolve_layer_config(rules, defaults, quantized, n) for n in names]
-    if len(set(cfgs)) != 1:
-        raise ValueError(f"fused layer {layer_name!r}: sub-layer configs differ: {cfgs}")
-    return cfgs[0]
+        members = [key for key, _ in rules if key.startswith(layer_name)]
+        if not members:
+            return resolve_layer_config(rules, defaults, quantized, layer_name)
+    resolved = {resolve_layer_config(rules, defaults, quantized, m) for m in members}
+    if len(resolved) != 1:
+        raise ValueError(f"fused layer {layer_name!r}: sub-layers resolve to {sorted(resolved)}")
+    return resolved.pop()
 

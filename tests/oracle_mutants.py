@@ -89,18 +89,18 @@ MUTANTS = {
     "init_clip_ignores_shrink": ("init_clip", "a = np.full((N, Gn), F32(cfg.minmax_shrink), F32)",
                                  "a = np.full((N, Gn), F32(1.0), F32)"),
     # per-layer configuration
-    "layer_pattern_prefix_match": ("resolve_layer_config", "if re.fullmatch(key, name):",
-                                   "if re.match(key, name):"),
+    "layer_pattern_prefix_match": ("_whole_name_match", "re.compile(key).fullmatch(name)",
+                                   "re.compile(key).match(name)"),
     "layer_exact_key_defaults_outside_set": ("resolve_layer_config",
-                                             'cfg.get("bits", bits if quantized else 16)',
-                                             'cfg.get("bits", bits)'),
-    "layer_plain_keys_as_patterns": ("resolve_layer_config",
-                                     "        if not any(c in REGEX_SPECIAL_CHARS for c in key):\n"
-                                     "            continue\n", ""),
-    "fused_configs_not_compared": ("resolve_fused_config", "if len(set(cfgs)) != 1:", "if False:"),
+                                             "return _merge(by_key[name], fallback)",
+                                             "return _merge(by_key[name], tuple(defaults))"),
+    "layer_plain_keys_as_patterns": ("_whole_name_match",
+                                     "    if REGEX_SPECIAL_CHARS.isdisjoint(key):\n        return False\n",
+                                     ""),
+    "fused_configs_not_compared": ("resolve_fused_config", "if len(resolved) != 1:", "if False:"),
     "fused_experts_not_collected": ("resolve_fused_config",
-                                    "names = [k for k, _ in rules if k.startswith(layer_name)]",
-                                    "names = []"),
+                                    "members = [key for key, _ in rules if key.startswith(layer_name)]",
+                                    "members = []"),
     # block forward (oracle/block_ref.py)
     "rmsnorm_sum_not_mean": ("block_ref.rmsnorm", "np.mean(x.astype(F64) ** 2", "np.sum(x.astype(F64) ** 2"),
     "rmsnorm_weight_dropped": ("block_ref.rmsnorm", " * np.asarray(w, F32))", ")"),
