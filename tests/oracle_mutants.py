@@ -26,6 +26,7 @@ MUTANTS = {
                                    "lo = alpha * wmin"),
     "sym_scale_halved": ("qparams", "s = (F32(2.0) * amax) / maxq", "s = amax / maxq"),
     "sym_zero_point": ("qparams", "F32(2 ** (bits - 1))", "F32(2 ** (bits - 1) - 1)"),
+    "hi_not_anchored": ("qparams", "hi = np.maximum(beta * wmax, F32(0.0))", "hi = beta * wmax"),
     # fake-quantization
     "round_half_up": ("fake_quant", "r = np.rint(u)", "r = np.floor(u + F32(0.5))"),
     "offset_after_rounding": ("fake_quant", "    u = t + V\n    r = np.rint(u)\n",
@@ -41,6 +42,8 @@ MUTANTS = {
     "residual_sign": ("forward_backward", "R = Yp - np.asarray(Yb, F64)",
                       "R = np.asarray(Yb, F64) - Yp"),
     "grad_transposed": ("forward_backward", "(dY.T @ X64)", "(X64.T @ dY)"),
+    "dY_not_rounded": ("forward_backward",
+                       "dY = bf16(R.astype(F32)).astype(F64) if amp else R", "dY = R"),
     # straight-through gradients
     "ste_no_mask": ("ste_grads", "gV = G64 * fq.s_e.astype(F64) * m", "gV = G64 * fq.s_e.astype(F64)"),
     "ste_scale_term_drops_t": ("ste_grads", "(qz - m * fq.t.astype(F64))", "qz"),
@@ -48,6 +51,7 @@ MUTANTS = {
     "ste_dlo_drops_zp_term": ("ste_grads", "dlo = -D / maxq - B / s64", "dlo = -D / maxq"),
     "ste_sym_routed_wrong": ("ste_grads", "        ga = np.where(to_alpha, damax",
                              "        to_alpha = ~to_alpha\n        ga = np.where(to_alpha, damax"),
+    "sym_tie_to_alpha": ("ste_grads", "np.asarray(wmin, F32)) > \\", "np.asarray(wmin, F32)) >= \\"),
     # SignSGD
     "sgn_of_zero_is_one": ("sgn", "(x > 0).astype(F32)", "(x >= 0).astype(F32)"),
     "offset_clamp_too_wide": ("signsgd_update", "F32(-0.5), F32(0.5)", "F32(-1.0), F32(1.0)"),

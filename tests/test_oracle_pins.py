@@ -231,6 +231,25 @@ def test_gram_loop_first_loss_matches_token_loop():
     assert r_g.best_loss == min(r_g.losses) and r_g.best_loss <= r_g.losses[0]
 
 
+def test_amp_rounds_dy_to_bf16_hand_value():
+    """amp=True ([LLMC] parameter table: mixed precision) rounds the residual to
+    bf16 before the gradient product, while the loss keeps it unrounded. One
+    token, one output, K = 2: X = [1, 0.5], Ŵ = [1, 0], Y = 2^-9, so
+    R = 1 - 2^-9 = 0.111111111b needs 9 significant bits; bf16 keeps 8, the
+    dropped bit is exactly half an ulp and the tie goes to the even neighbour
+    1.0. By hand: L = (1 - 2^-9)^2, G = (2/(T·N))·bf16(R)·X = 2·[1, 0.5] = [2, 1]
+    (unrounded it would be [1.99609375, 0.998046875])."""
+    X = np.array([[1.0, 0.5]], F32)
+    Wq = np.array([[1.0, 0.0]], F32)
+    Y = np.array([[2.0 ** -9]], F32)
+    L, G, loss_sum = O.forward_backward(X, Y, Wq, amp=True)
+    assert L == (1.0 - 2.0 ** -9) ** 2 and loss_sum == L
+    np.testing.assert_array_equal(G, np.array([[2.0, 1.0]]))
+    # amp=False keeps the residual exact
+    _, G2, _ = O.forward_backward(X, Y, Wq, amp=False)
+    np.testing.assert_array_equal(G2, np.array([[1.99609375, 0.998046875]]))
+
+
 def test_amp_close_to_exact():
     W, X, Y, wmin, wmax, a, b, V = _problem(K=64, T=64)
     qp = O.qparams(wmin, wmax, a, b, 3, False)
@@ -294,6 +313,33 @@ def test_ste_grads_match_autograd(sym, bits):
     np.testing.assert_allclose(ga, ra, rtol=1e-4, atol=1e-6 * np.abs(ra).max())
     np.testing.assert_allclose(gb, rb, rtol=1e-4, atol=1e-6 * np.abs(rb).max())
     assert np.abs(ga).max() > 0 and np.abs(gb).max() > 0
+
+
+def test_ste_sym_tie_goes_to_beta_hand_value():
+    """Symmetric grid with |alpha·wmin| = |beta·wmax|: the clip-factor gradient
+    goes to beta alone (the pages are silent; max() has no unique derivative
+    at a tie, and the reading taken is that the max side wins). 2-bit sym,
+    one group W = [-0.5, 0, 0.25, 0.5], alpha = beta = 1: amax = 0.5,
+    s = 2·0.5/3 (float32 0.33333334), zp = 2; t = W/s = [-1.5, 0, 0.75, 1.5];
+    rint = [-2, 0, 1, 2]; c = [0, 2, 3, 4]; q = [0, 2, 3, 3]; m = [1, 1, 1, 0].
+    With G = 1 everywhere: A = Σ G·((q - zp) - m·t) = (-2 + 1.5) + 0 +
+    (1 - 0.75) + 1 = 0.75; dL/damax = 2A/maxq = 0.5; so dL/dbeta = 0.5·|wmax| =
+    0.25 and dL/dalpha = 0; dL/dV = G·s·m."""
+    W = np.array([[-0.5, 0.0, 0.25, 0.5]], F32)
+    V = np.zeros_like(W)
+    a = np.ones((1, 1), F32)
+    b = np.ones((1, 1), F32)
+    wmin, wmax = O.group_minmax(W, 4)
+    qp = O.qparams(wmin, wmax, a, b, 2, True)
+    fq = O.fake_quant(W, V, qp, 2, 4)
+    np.testing.assert_array_equal(fq.q[0], [0, 2, 3, 3])
+    np.testing.assert_array_equal(fq.m[0], [True, True, True, False])
+    G = np.ones((1, 4))
+    gV, ga, gb = O.ste_grads(G, W, fq, qp, wmin, wmax, a, b, 2, True, 4)
+    assert ga[0, 0] == 0.0
+    assert abs(gb[0, 0] - 0.25) < 1e-7
+    s = float(F32(1.0) / F32(3.0))
+    np.testing.assert_allclose(gV[0], [s, s, s, 0.0], rtol=1e-7)
 
 
 # ------------------------------------------------------------------ S9
