@@ -29,8 +29,11 @@ EXPORTS = (
     "ar_gram_workspace_size", "ar_gram_step_workspace_size", "ar_tune_step_gram",
     "ar_tune_linear_gram", "ar_init_clip", "ar_resolve_layer_config", "ar_resolve_fused_config",
     "ar_dequant_gemm_workspace_size", "ar_dequant_gemm", "ar_block_workspace_size",
-    "ar_block_forward", "ar_tune_block", "ar_attention",
+    "ar_block_forward", "ar_tune_block", "ar_attention", "ar_tune_step_noalloc",
 )
+
+# fixed scratch of ar_tune_step_noalloc per GPU (AR_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 
 class ArConfig(ctypes.Structure):
@@ -112,6 +115,8 @@ def _load():
         "ar_fakequant_fwd": [cfgp, i32, vp, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp],
         "ar_tune_step": [cfgp, ctypes.POINTER(ArState), vp, vp, i32, i64, vp, vp, vp, vp, i32,
                          vp, sz, vp],
+        "ar_tune_step_noalloc": [cfgp, ctypes.POINTER(ArState), vp, vp, i32, i64, vp, vp, vp,
+                                 vp, i32, vp],
         "ar_tune_linear": [cfgp, i32, vp, i64, i64, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                            vp, sz, ctypes.POINTER(ArKernelTimes), vp],
         "ar_gram_workspace_size": [cfgp, i32, i64, i64, i32, ctypes.POINTER(sz)],
@@ -307,11 +312,12 @@ def fakequant_fwd(W, V, alpha, beta, cfg: Config, stream=None):
 
 
 def tune_step(W, V, alpha, beta, Xb, Yb, cfg: Config, *, best=None, want_grads=True,
-              apply_update=True, workspace=None, stream=None, gram=False):
+              apply_update=True, workspace=None, stream=None, gram=False, noalloc=False):
     """One SignSGD step in place on (V, alpha, beta). ``best`` is an optional
     tuple (best_V, best_alpha, best_beta, best_loss[1]). Returns
     (loss[1] device tensor, gV, galpha, gbeta) with grads None unless wanted.
-    ``gram`` selects ar_tune_step_gram."""
+    ``gram`` selects ar_tune_step_gram; ``noalloc`` selects
+    ar_tune_step_noalloc (no workspace: the library's fixed scratch)."""
     torch = _torch()
     _dev(W, V, alpha, beta, Xb, Yb)
     N, K = W.shape
@@ -319,7 +325,9 @@ def tune_step(W, V, alpha, beta, Xb, Yb, cfg: Config, *, best=None, want_grads=T
     if Xb.dtype != torch.bfloat16 or Xb.shape[1] != K or tuple(Yb.shape) != (Tb, N):
         raise ValueError("Xb must be bf16 [Tb, K] and Yb [Tb, N]")
     ydt = _dt(Yb)
-    if workspace is None:
+    if noalloc and (gram or workspace is not None):
+        raise ValueError("noalloc takes no workspace and has no Gram form")
+    if workspace is None and not noalloc:
         need = gram_step_workspace_size(cfg, _dt(W), N, K, Tb, ydt) if gram else \
             step_workspace_size(cfg, N, K, Tb, ydt)
         workspace = torch.empty(need, dtype=torch.uint8, device=W.device)
@@ -332,6 +340,12 @@ def tune_step(W, V, alpha, beta, Xb, Yb, cfg: Config, *, best=None, want_grads=T
                  None if bV is None else bV.data_ptr(), None if bA is None else bA.data_ptr(),
                  None if bB is None else bB.data_ptr(), None if bL is None else bL.data_ptr())
     cc = cfg.c()
+    if noalloc:
+        _check(lib.ar_tune_step_noalloc(ctypes.byref(cc), ctypes.byref(st), _ptr(Xb), _ptr(Yb),
+                                        ydt, Tb, _ptr(loss), _ptr(gV), _ptr(ga), _ptr(gb),
+                                        int(apply_update), _stream(stream)),
+               "ar_tune_step_noalloc")
+        return loss, gV, ga, gb
     fn, name = (lib.ar_tune_step_gram, "ar_tune_step_gram") if gram else \
         (lib.ar_tune_step, "ar_tune_step")
     _check(fn(ctypes.byref(cc), ctypes.byref(st), _ptr(Xb), _ptr(Yb), ydt, Tb, _ptr(loss),

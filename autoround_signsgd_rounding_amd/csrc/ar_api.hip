@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "ar_blocked.h"
@@ -351,6 +352,60 @@ ar_status stage_gram_weight(const GramWs& w, const GramSizes& q, int wdt, const 
   return AR_OK;
 }
 
+// Every check of ar_tune_step except the workspace's; *need = its workspace bytes.
+ar_status check_step(const ar_config* c, const ar_state* s, const uint16_t* Xb, const void* Yb,
+                     int32_t ydt, int64_t Tb, const float* loss_out, const float* gV, int* g,
+                     size_t* need) {
+  if (!s) return AR_ERR_INVALID_ARG;
+  AR_TRY(check_quant(c, s->N, s->K, g));
+  AR_TRY(check_tune(c));
+  if (!dtype_ok(s->wdt) || !dtype_ok(ydt)) return AR_ERR_UNSUPPORTED;
+  if (*g == 0 || Tb <= 0 || Tb % 8 != 0 || Tb >= kMaxLd) return AR_ERR_SHAPE;
+  const int nbest = (s->best_V != nullptr) + (s->best_alpha != nullptr) +
+                    (s->best_beta != nullptr) + (s->best_loss != nullptr);
+  if (nbest != 0 && nbest != 4) return AR_ERR_INVALID_ARG;
+  if (!s->W || !s->V || !s->alpha || !s->beta || !Xb || !Yb || !loss_out)
+    return AR_ERR_INVALID_ARG;
+  if (!a16(s->W) || !a16(s->V) || !a16(s->best_V) || !a16(Xb) || !a16(Yb) || !a16(gV))
+    return AR_ERR_INVALID_ARG;
+  carve_step(nullptr, s->N, s->K, Tb, ydt, need);
+  return AR_OK;
+}
+
+// One SignSGD step of ar_tune_step on validated arguments, scratch at ws.
+// Everything the step reads from ws is written first by the same call (the
+// staged minibatch, Ŵ with its zero padding, the products, the loss
+// partials and the improvement flag), so ws may hold anything on entry.
+ar_status run_step(const ar_config* c, const ar_state* s, int g, const uint16_t* Xb,
+                   const void* Yb, int32_t ydt, int64_t Tb, float* loss_out, float* gV,
+                   float* galpha, float* gbeta, int32_t apply_update, void* ws, hipStream_t st) {
+  const int64_t N = s->N, K = s->K;
+  size_t need;
+  StepWs w = carve_step(ws, N, K, Tb, ydt, &need);
+  const BlkSizes z(N, K, Tb);
+
+  // stage the minibatch into the blocked GEMM layouts, Ŵ of the current state
+  AR_TRY(ar_launch_stage_x(Xb, w.XTB, w.XB, 1, Tb, K, z.nkbT, z.nkbK, st));
+  AR_TRY(ar_launch_block_transpose(Yb, w.YB, 1, Tb, N, z.nkbT, (int)dsize(ydt), st));
+  AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(w.WB), 0.0f, z.wb / 2, st));
+  AR_TRY(ar_launch_fakequant(s->wdt, s->W, s->V, s->alpha, s->beta, init_of(c), N, K, g,
+                             grid_of(c), AR_BF16, w.WB, z.nkbK, nullptr, nullptr, nullptr, st));
+  return enqueue_step(c, s->wdt, s->W, N, K, g, w.XB, w.XTB, w.YB, ydt, Tb, w.WB, w.dyB, w.G,
+                      w.partials, w.flag, loss_out, nullptr, s->best_loss, s->V, s->alpha,
+                      s->beta, s->best_V, s->best_alpha, s->best_beta, gV, galpha, gbeta,
+                      apply_update != 0, false, st, nullptr);
+}
+
+// Scratch of ar_tune_step_noalloc: a fixed array in every GPU's memory, held
+// until the process ends. In host code `scratch` is a host-side stand-in, not
+// a device address; the address of a device's copy comes from
+// hipGetSymbolAddress with that device current, once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+ar_status scratch_of_current_device(void** out);
+
 ArGramArgs gram_args(const ar_config* c, int wdt, const void* W, int64_t N, int64_t K, int g,
                      int64_t Tb) {
   ArGramArgs a{};
@@ -361,6 +416,23 @@ ArGramArgs gram_args(const ar_config* c, int wdt, const void* W, int64_t N, int6
   return a;
 }
 
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[AR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+ar_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return AR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return AR_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return AR_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -390,7 +462,7 @@ const char* ar_status_string(int32_t s) {
     case AR_ERR_INVALID_ARG: return "invalid argument (null pointer, bad hyper-parameter or misaligned pointer)";
     case AR_ERR_UNSUPPORTED: return "unsupported (bits must be 2, 3, 4 or 8; group_size a multiple of 8; dtype f32/bf16)";
     case AR_ERR_SHAPE: return "shape constraint violated";
-    case AR_ERR_WORKSPACE: return "workspace too small";
+    case AR_ERR_WORKSPACE: return "workspace too small (ar_tune_step_noalloc: the problem needs more than its fixed scratch)";
     case AR_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -459,37 +531,27 @@ ar_status ar_tune_step(const ar_config* c, const ar_state* s, const uint16_t* Xb
                        int32_t ydt, int64_t Tb, float* loss_out, float* gV, float* galpha,
                        float* gbeta, int32_t apply_update, void* ws, size_t ws_bytes,
                        void* stream) {
-  if (!s) return AR_ERR_INVALID_ARG;
   int g;
-  AR_TRY(check_quant(c, s->N, s->K, &g));
-  AR_TRY(check_tune(c));
-  if (!dtype_ok(s->wdt) || !dtype_ok(ydt)) return AR_ERR_UNSUPPORTED;
-  if (g == 0 || Tb <= 0 || Tb % 8 != 0 || Tb >= kMaxLd) return AR_ERR_SHAPE;
-  const int nbest = (s->best_V != nullptr) + (s->best_alpha != nullptr) +
-                    (s->best_beta != nullptr) + (s->best_loss != nullptr);
-  if (nbest != 0 && nbest != 4) return AR_ERR_INVALID_ARG;
-  if (!s->W || !s->V || !s->alpha || !s->beta || !Xb || !Yb || !loss_out || !ws)
-    return AR_ERR_INVALID_ARG;
-  if (!a16(s->W) || !a16(s->V) || !a16(s->best_V) || !a16(Xb) || !a16(Yb) || !a16(gV) || !a16(ws))
-    return AR_ERR_INVALID_ARG;
-  const int64_t N = s->N, K = s->K;
   size_t need;
-  carve_step(nullptr, N, K, Tb, ydt, &need);
+  AR_TRY(check_step(c, s, Xb, Yb, ydt, Tb, loss_out, gV, &g, &need));
+  if (!ws || !a16(ws)) return AR_ERR_INVALID_ARG;
   if (ws_bytes < need) return AR_ERR_WORKSPACE;
-  StepWs w = carve_step(ws, N, K, Tb, ydt, &need);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const BlkSizes z(N, K, Tb);
+  return run_step(c, s, g, Xb, Yb, ydt, Tb, loss_out, gV, galpha, gbeta, apply_update, ws,
+                  static_cast<hipStream_t>(stream));
+}
 
-  // stage the minibatch into the blocked GEMM layouts, Ŵ of the current state
-  AR_TRY(ar_launch_stage_x(Xb, w.XTB, w.XB, 1, Tb, K, z.nkbT, z.nkbK, st));
-  AR_TRY(ar_launch_block_transpose(Yb, w.YB, 1, Tb, N, z.nkbT, (int)dsize(ydt), st));
-  AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(w.WB), 0.0f, z.wb / 2, st));
-  AR_TRY(ar_launch_fakequant(s->wdt, s->W, s->V, s->alpha, s->beta, init_of(c), N, K, g,
-                             grid_of(c), AR_BF16, w.WB, z.nkbK, nullptr, nullptr, nullptr, st));
-  return enqueue_step(c, s->wdt, s->W, N, K, g, w.XB, w.XTB, w.YB, ydt, Tb, w.WB, w.dyB, w.G,
-                      w.partials, w.flag, loss_out, nullptr, s->best_loss, s->V, s->alpha,
-                      s->beta, s->best_V, s->best_alpha, s->best_beta, gV, galpha, gbeta,
-                      apply_update != 0, false, st, nullptr);
+ar_status ar_tune_step_noalloc(const ar_config* c, const ar_state* s, const uint16_t* Xb,
+                               const void* Yb, int32_t ydt, int64_t Tb, float* loss_out,
+                               float* gV, float* galpha, float* gbeta, int32_t apply_update,
+                               void* stream) {
+  int g;
+  size_t need;
+  AR_TRY(check_step(c, s, Xb, Yb, ydt, Tb, loss_out, gV, &g, &need));
+  if (need > AR_NOALLOC_SCRATCH_BYTES) return AR_ERR_WORKSPACE;
+  void* ws = nullptr;
+  AR_TRY(scratch_of_current_device(&ws));
+  return run_step(c, s, g, Xb, Yb, ydt, Tb, loss_out, gV, galpha, gbeta, apply_update, ws,
+                  static_cast<hipStream_t>(stream));
 }
 
 ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t N, int64_t K,

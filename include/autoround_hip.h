@@ -168,6 +168,24 @@ ar_status ar_tune_step(const ar_config* cfg, const ar_state* state, const uint16
                        float* galpha, float* gbeta, int32_t apply_update, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* ar_tune_step for callers that cannot allocate device memory (code under HIP
+   graph capture, tight loops, harnesses that forbid allocation): the same
+   arguments without (ws, ws_bytes), and the same kernels, results and errors.
+   Its scratch is a fixed array of AR_NOALLOC_SCRATCH_BYTES in each GPU's
+   memory, set up on the first call on that device (the device current at the
+   call, which must be the stream's) and held until the process ends. A problem
+   whose ar_step_workspace_size exceeds AR_NOALLOC_SCRATCH_BYTES returns
+   AR_ERR_WORKSPACE before anything is enqueued. The call makes no device
+   allocation. Every call on one GPU shares that GPU's array: calls that may
+   overlap on one GPU (other streams, other host threads) race and must be
+   serialised by the caller. Each call writes every part of the array it reads
+   before reading it, so what an earlier call left there does not matter. */
+#define AR_NOALLOC_SCRATCH_BYTES ((size_t)64 * 1024 * 1024)
+ar_status ar_tune_step_noalloc(const ar_config* cfg, const ar_state* state, const uint16_t* Xb,
+                               const void* Yb, int32_t ydt, int64_t Tb, float* loss_out,
+                               float* gV, float* galpha, float* gbeta, int32_t apply_update,
+                               void* stream);
+
 /* The whole per-Linear tuning loop ([LLMC] tuning loop with best-loss snapshot):
    V = 0, alpha and beta from ar_init_clip; step i uses minibatch b = i mod
    (nsamples/batch_samples), i.e. rows [b*Tb, (b+1)*Tb) of X and Y with
