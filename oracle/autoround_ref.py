@@ -257,6 +257,8 @@ def forward_backward(Xb, Yb, what, *, amp: bool = True, n_scale: int | None = No
     """
     T = Xb.shape[0]
     N = what.shape[0]
+    if T == 0 or N == 0:
+        raise ValueError("the loss is a mean over tokens and outputs: needs T > 0 and N > 0")
     Nn = N if n_scale is None else n_scale
     X64 = np.asarray(Xb, F64)
     Wq = bf16(what) if amp else np.asarray(what, F32)

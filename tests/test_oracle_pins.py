@@ -250,6 +250,14 @@ def test_amp_rounds_dy_to_bf16_hand_value():
     np.testing.assert_array_equal(G2, np.array([[1.99609375, 0.998046875]]))
 
 
+def test_empty_minibatch_is_rejected():
+    """The loss is a mean over the minibatch ([LLMC] tuning loop, ``.mean()``):
+    an empty minibatch has none, and the oracle refuses it instead of
+    dividing by zero."""
+    with pytest.raises(ValueError):
+        O.forward_backward(np.zeros((0, 8), F32), np.zeros((0, 4), F32), np.zeros((4, 8), F32))
+
+
 def test_amp_close_to_exact():
     W, X, Y, wmin, wmax, a, b, V = _problem(K=64, T=64)
     qp = O.qparams(wmin, wmax, a, b, 3, False)
@@ -426,6 +434,43 @@ def test_steps_cycle_through_minibatches():
         return X, Y
     O.tune_linear(W, minibatch, 3, _cfg(bits=4, group_size=16, iters=8))
     assert seen == [0, 1, 2, 0, 1, 2, 0, 1]
+
+
+def test_nan_target_never_snapshotted_and_moves_nothing():
+    """A NaN in one minibatch's targets: every step on that minibatch has a NaN
+    loss, which the strict < of the best-state snapshot never takes, and the
+    NaN reaches only the gradient row of the NaN's output, whose sign is taken
+    as 0, so that row does not move on those steps while the other rows do.
+    The returned state is finite. (The pages' loop reads each batch loss on the
+    host and leaves non-finite data open; these are the readings the loop
+    follows: sgn(NaN) = 0, snapshot on a strictly lower loss.)"""
+    rng = np.random.default_rng(3)
+    N, K, T, nb = 4, 16, 12, 3
+    W = (rng.standard_normal((N, K)) * 0.02).astype(F32)
+    Xs = [rng.standard_normal((T, K)).astype(F32) for _ in range(nb)]
+    Ys = [(x.astype(np.float64) @ W.astype(np.float64).T).astype(F32) for x in Xs]
+    Ys[1] = Ys[1].copy()
+    Ys[1][5, 2] = np.nan                      # output row 2, minibatch 1
+    cfg = _cfg(bits=3, group_size=8, iters=7, minmax_lr=0.01)
+    rows = []
+
+    def on_step(i, r):
+        rows.append(r)
+    res = O.tune_linear(W, lambda b: (Xs[b], Ys[b]), nb, cfg, on_step=on_step)
+    losses = np.array(res.losses)
+    nan_steps = [i for i in range(cfg.iters) if i % nb == 1]
+    assert np.all(np.isnan(losses[nan_steps]))
+    assert np.all(np.isfinite(np.delete(losses, nan_steps)))
+    assert res.best_step not in nan_steps and res.best_loss == np.nanmin(losses)
+    for arr in (res.V, res.alpha, res.beta, res.what, res.scale):
+        assert np.all(np.isfinite(arr))
+    V = np.zeros((N, K), F32)
+    for i, r in enumerate(rows):
+        if i in nan_steps:
+            assert np.all(np.isnan(r.gV[2])) and np.all(np.isfinite(np.delete(r.gV, 2, 0)))
+            np.testing.assert_array_equal(r.V[2], V[2])
+            assert not np.array_equal(np.delete(r.V, 2, 0), np.delete(V, 2, 0))
+        V = r.V
 
 
 def test_brute_force_2x4():
