@@ -19,7 +19,7 @@ SUPPORTED_BITS = (2, 3, 4, 8)
 
 STATUS = {
     0: "AR_OK", 1: "AR_ERR_INVALID_ARG", 2: "AR_ERR_UNSUPPORTED", 3: "AR_ERR_SHAPE",
-    4: "AR_ERR_WORKSPACE", 6: "AR_ERR_HIP",
+    4: "AR_ERR_WORKSPACE", 5: "AR_ERR_NONFINITE", 6: "AR_ERR_HIP",
 }
 
 # every symbol declared in include/autoround_hip.h
@@ -44,7 +44,7 @@ class ArConfig(ctypes.Structure):
         ("lr", ctypes.c_float), ("minmax_lr", ctypes.c_float),
         ("minmax_shrink", ctypes.c_float), ("clip_lo", ctypes.c_float),
         ("clip_hi", ctypes.c_float), ("init_scale", ctypes.c_int32),
-        ("mse_grid", ctypes.c_int32),
+        ("mse_grid", ctypes.c_int32), ("check_finite", ctypes.c_int32),
     ]
 
 
@@ -184,6 +184,7 @@ class Config:
     clip_hi: float = 1.0
     init: str = "minmax"       # initial scale: "minmax" or "mse"
     mse_grid: int = 100
+    check_finite: bool = False  # scan the inputs first; NaN/Inf -> AR_ERR_NONFINITE
 
     def c(self) -> ArConfig:
         if self.init not in ("minmax", "mse"):
@@ -192,7 +193,7 @@ class Config:
                         self.batch_samples, self.iters, self.lr,
                         -1.0 if self.minmax_lr is None else self.minmax_lr,
                         self.minmax_shrink, self.clip_lo, self.clip_hi,
-                        1 if self.init == "mse" else 0, self.mse_grid)
+                        1 if self.init == "mse" else 0, self.mse_grid, int(self.check_finite))
 
     def G(self, K: int) -> int:
         return 1 if self.group_size == -1 else K // self.group_size
@@ -232,6 +233,33 @@ def _dev(*ts):
                 raise ValueError("tensors must be contiguous")
 
 
+def _need(t, name, shape, dtypes):
+    """ValueError unless t is a contiguous GPU tensor of this shape and one of
+    these dtypes (the library indexes every buffer by the shapes it is given,
+    so a mismatch would read or write out of bounds)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    _dev(t)
+    if not isinstance(dtypes, tuple):
+        dtypes = (dtypes,)
+    if tuple(t.shape) != tuple(shape) or t.dtype not in dtypes:
+        want = "/".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} must be {want} {list(shape)}, got {t.dtype} {list(t.shape)}")
+
+
+def _weight(W, name="W"):
+    """(N, K) of a 2-D float32 / bf16 weight on the GPU."""
+    torch = _torch()
+    if W is None or W.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D [N, K] tensor")
+    _need(W, name, W.shape, (torch.float32, torch.bfloat16))
+    return W.shape
+
+
+def _groups(group_size: int, K: int) -> int:
+    return 1 if group_size == -1 else (K // group_size if group_size > 0 else 0)
+
+
 def workspace_size(cfg: Config, N: int, K: int, ydtype) -> int:
     out = ctypes.c_size_t()
     cc = cfg.c()
@@ -267,8 +295,7 @@ def gram_step_workspace_size(cfg: Config, wdt: int, N: int, K: int, Tb: int, ydt
 def init_clip(W, cfg: Config, stream=None):
     """Initial clip factors (alpha, beta) [N, G] float32 (Min-Max shrink or MSE search)."""
     torch = _torch()
-    _dev(W)
-    N, K = W.shape
+    N, K = _weight(W)
     G = cfg.G(K)
     alpha = torch.empty((N, G), dtype=torch.float32, device=W.device)
     beta = torch.empty_like(alpha)
@@ -281,8 +308,7 @@ def init_clip(W, cfg: Config, stream=None):
 def rtn_quant(W, cfg: Config, stream=None, want_wq: bool = True):
     """RTN codes [N,K] u8, scale [N,G] f32, zp [N,G] u8, Wq [N,K] (W's dtype)."""
     torch = _torch()
-    _dev(W)
-    N, K = W.shape
+    N, K = _weight(W)
     G = cfg.G(K)
     codes = torch.empty((N, K), dtype=torch.uint8, device=W.device)
     scale = torch.empty((N, G), dtype=torch.float32, device=W.device)
@@ -297,9 +323,11 @@ def rtn_quant(W, cfg: Config, stream=None, want_wq: bool = True):
 def fakequant_fwd(W, V, alpha, beta, cfg: Config, stream=None):
     """bf16 Ŵ [N,K], codes [N,K] u8, scale [N,G] f32, zp [N,G] u8."""
     torch = _torch()
-    _dev(W, V, alpha, beta)
-    N, K = W.shape
+    N, K = _weight(W)
     G = cfg.G(K)
+    _need(V, "V", (N, K), torch.float32)
+    _need(alpha, "alpha", (N, G), torch.float32)
+    _need(beta, "beta", (N, G), torch.float32)
     Wq = torch.empty((N, K), dtype=torch.bfloat16, device=W.device)
     codes = torch.empty((N, K), dtype=torch.uint8, device=W.device)
     scale = torch.empty((N, G), dtype=torch.float32, device=W.device)
@@ -319,11 +347,24 @@ def tune_step(W, V, alpha, beta, Xb, Yb, cfg: Config, *, best=None, want_grads=T
     ``gram`` selects ar_tune_step_gram; ``noalloc`` selects
     ar_tune_step_noalloc (no workspace: the library's fixed scratch)."""
     torch = _torch()
-    _dev(W, V, alpha, beta, Xb, Yb)
-    N, K = W.shape
+    N, K = _weight(W)
+    G = cfg.G(K)
+    if Xb is None or Xb.dim() != 2:
+        raise ValueError("Xb must be a 2-D [Tb, K] tensor")
     Tb = Xb.shape[0]
-    if Xb.dtype != torch.bfloat16 or Xb.shape[1] != K or tuple(Yb.shape) != (Tb, N):
-        raise ValueError("Xb must be bf16 [Tb, K] and Yb [Tb, N]")
+    _need(Xb, "Xb", (Tb, K), torch.bfloat16)
+    _need(Yb, "Yb", (Tb, N), (torch.float32, torch.bfloat16))
+    _need(V, "V", (N, K), torch.float32)
+    _need(alpha, "alpha", (N, G), torch.float32)
+    _need(beta, "beta", (N, G), torch.float32)
+    if best is not None:
+        bV, bA, bB, bL = best
+        _need(bV, "best_V", (N, K), torch.float32)
+        _need(bA, "best_alpha", (N, G), torch.float32)
+        _need(bB, "best_beta", (N, G), torch.float32)
+        _need(bL, "best_loss", (1,), torch.float32)
+    if workspace is not None:
+        _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
     ydt = _dt(Yb)
     if noalloc and (gram or workspace is not None):
         raise ValueError("noalloc takes no workspace and has no Gram form")
@@ -374,10 +415,12 @@ def tune_linear(W, X, Y, cfg: Config, *, want_state=True, want_wq=False, timed=F
     kernels of every ``time_every``-th step. ``gram`` selects
     ar_tune_linear_gram."""
     torch = _torch()
-    _dev(W, X, Y)
-    N, K = W.shape
-    if X.dtype != torch.bfloat16:
-        raise ValueError("X must be bf16")
+    N, K = _weight(W)
+    M = cfg.nsamples * cfg.seqlen
+    _need(X, "X", (M, K), torch.bfloat16)
+    _need(Y, "Y", (M, N), (torch.float32, torch.bfloat16))
+    if workspace is not None:
+        _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
     G = cfg.G(K)
     ydt = _dt(Y)
     dev = W.device
@@ -419,15 +462,25 @@ def dequant_gemm(X, qweight, qzeros, scale, bits: int, group_size: int, N: int, 
     bf16; qzeros None for the symmetric grid; scale [N, G] float32. ``out`` and
     ``workspace`` may be given to avoid allocations."""
     torch = _torch()
-    _dev(X, qweight, qzeros, scale, out)
+    if X is None or X.dim() != 2:
+        raise ValueError("X must be a 2-D [M, K] tensor")
     M, K = X.shape
-    if X.dtype != torch.bfloat16:
-        raise ValueError("X must be bf16")
+    _need(X, "X", (M, K), torch.bfloat16)
+    if bits not in SUPPORTED_BITS:
+        raise ValueError(f"bits must be one of {SUPPORTED_BITS}")
+    G = _groups(group_size, K)
+    _need(qweight, "qweight", (K * bits // 32, N), torch.int32)
+    if qzeros is not None:
+        _need(qzeros, "qzeros", (G, N * bits // 32), torch.int32)
+    _need(scale, "scale", (N, G), torch.float32)
     if out is None:
         out_dtype = torch.float32 if out_dtype is None else out_dtype
         Y = torch.empty((M, N), dtype=out_dtype, device=X.device)
     else:
+        _need(out, "out", (M, N), (torch.float32, torch.bfloat16))
         Y = out
+    if workspace is not None:
+        _need(workspace, "workspace", (workspace.numel(),), torch.uint8)
     if workspace is None:
         need = dequant_gemm_workspace_size(bits, group_size, M, N, K)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
@@ -441,8 +494,14 @@ def pack(codes, zp, bits: int, stream=None, out=None):
     """qweight [K*bits/32, N] int32 and qzeros [G, N*bits/32] int32 (or None).
     ``out`` = (qweight, qzeros) writes into given tensors instead."""
     torch = _torch()
-    _dev(codes, zp)
+    if codes is None or codes.dim() != 2:
+        raise ValueError("codes must be a 2-D [N, K] uint8 tensor")
     N, K = codes.shape
+    _need(codes, "codes", (N, K), torch.uint8)
+    if zp is not None:
+        if zp.dim() != 2 or zp.shape[0] != N:
+            raise ValueError("zp must be a 2-D [N, G] uint8 tensor")
+        _need(zp, "zp", (N, zp.shape[1]), torch.uint8)
     G = 0 if zp is None else zp.shape[1]
     if out is not None:
         qw, qz = out
@@ -463,7 +522,11 @@ def pack(codes, zp, bits: int, stream=None, out=None):
 
 def unpack(qweight, qzeros, bits: int, N: int, K: int, G: int, stream=None):
     torch = _torch()
-    _dev(qweight, qzeros)
+    if bits not in SUPPORTED_BITS:
+        raise ValueError(f"bits must be one of {SUPPORTED_BITS}")
+    _need(qweight, "qweight", (K * bits // 32, N), torch.int32)
+    if qzeros is not None:
+        _need(qzeros, "qzeros", (G, N * bits // 32), torch.int32)
     codes = torch.empty((N, K), dtype=torch.uint8, device=qweight.device)
     zp = torch.empty((N, G), dtype=torch.uint8, device=qweight.device) if qzeros is not None \
         else None
@@ -500,10 +563,16 @@ def resolve_fused_config(rules, defaults, quantized: bool, layer_name: str, sub_
     arr = _rules(rules)
     d = ArLayerQConfig(*[int(x) for x in defaults])
     out = ArLayerQConfig()
-    subs = list(sub_names or [])
-    names = (ctypes.c_char_p * max(len(subs), 1))(*[n.encode() for n in subs])
+    # None selects the fused-expert rule (sub-layers from the rule keys); an
+    # explicit list, even an empty one, is the sub-layer set itself
+    if sub_names is None:
+        names, nsub = None, 0
+    else:
+        subs = list(sub_names)
+        names = (ctypes.c_char_p * max(len(subs), 1))(*[n.encode() for n in subs])
+        nsub = len(subs)
     _check(lib.ar_resolve_fused_config(arr, len(rules), ctypes.byref(d), int(quantized),
-                                       layer_name.encode(), names, len(subs),
+                                       layer_name.encode(), names, nsub,
                                        ctypes.byref(out)), "ar_resolve_fused_config")
     return out.bits, out.group_size, bool(out.sym)
 
@@ -513,8 +582,23 @@ def block_dims(D, H, F, seqlen, nsamples, rms_eps=1e-6, rope_theta=10000.0) -> A
     return ArBlockDims(D, H, F, seqlen, nsamples, rms_eps, rope_theta)
 
 
-def _block_weights(W: dict, norms):
-    _dev(*W.values(), *norms)
+def _block_shapes(dims: ArBlockDims):
+    """[out, in] of each Linear of the block and the token count."""
+    D, F = dims.hidden, dims.inter
+    shapes = {"q_proj": (D, D), "k_proj": (D, D), "v_proj": (D, D), "o_proj": (D, D),
+              "gate_proj": (F, D), "up_proj": (F, D), "down_proj": (D, F)}
+    return shapes, dims.nsamples * dims.seqlen
+
+
+def _block_weights(W: dict, norms, dims: ArBlockDims):
+    torch = _torch()
+    shapes, _ = _block_shapes(dims)
+    for n in BLOCK_LINEARS:
+        _need(W.get(n), n, shapes[n], torch.bfloat16)
+    if len(norms) != 2:
+        raise ValueError("norms = (attention norm, MLP norm)")
+    for i, t in enumerate(norms):
+        _need(t, f"norms[{i}]", (dims.hidden,), torch.bfloat16)
     return ArBlockWeights(*[W[n].data_ptr() for n in BLOCK_LINEARS],
                           norms[0].data_ptr(), norms[1].data_ptr())
 
@@ -523,8 +607,8 @@ def block_forward(h, W: dict, norms, dims: ArBlockDims, stream=None):
     """The decoder block's forward (ar_block_forward): h [M, D] bf16, W maps
     the Linear names to bf16 [out, in] tensors, norms = (attention, MLP) bf16 [D]."""
     torch = _torch()
-    _dev(h)
-    bw = _block_weights(W, norms)
+    _need(h, "h", (_block_shapes(dims)[1], dims.hidden), torch.bfloat16)
+    bw = _block_weights(W, norms, dims)
     need = ctypes.c_size_t()
     _check(lib.ar_block_workspace_size(None, ctypes.byref(dims), ctypes.byref(need)),
            "ar_block_workspace_size")
@@ -539,9 +623,13 @@ def attention(q, k, v, dims: ArBlockDims, out=None, stream=None):
     """The block's causal attention step (ar_attention) on rotated q, k and v
     [nsamples·seqlen, hidden] bf16; returns out of the same shape."""
     torch = _torch()
-    _dev(q, k, v, out)
+    shape = (_block_shapes(dims)[1], dims.hidden)
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, nm, shape, torch.bfloat16)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _need(out, "out", shape, torch.bfloat16)
     _check(lib.ar_attention(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
                             _stream(stream)), "ar_attention")
     return out
@@ -552,9 +640,12 @@ def tune_block(h, W: dict, norms, dims: ArBlockDims, cfg: Config, *, quanted_inp
     """Sequential tuning of the block's Linears (ar_tune_block). Returns a dict
     name -> (codes, scale, zp, Wq, losses) and the block outputs (fp, quantized)."""
     torch = _torch()
-    _dev(h, h_q)
+    shape = (_block_shapes(dims)[1], dims.hidden)
+    _need(h, "h", shape, torch.bfloat16)
+    if h_q is not None:
+        _need(h_q, "h_q", shape, torch.bfloat16)
     dev = h.device
-    bw = _block_weights(W, norms)
+    bw = _block_weights(W, norms, dims)
     cc = cfg.c()
     need = ctypes.c_size_t()
     _check(lib.ar_block_workspace_size(ctypes.byref(cc), ctypes.byref(dims),

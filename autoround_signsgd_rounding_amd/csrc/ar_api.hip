@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -60,6 +61,7 @@ ar_status check_quant(const ar_config* c, int64_t N, int64_t K, int* g) {
   if (c->group_size != -1 && c->group_size <= 0) return AR_ERR_INVALID_ARG;
   if (!finite(c->minmax_shrink) || c->minmax_shrink <= 0.0f) return AR_ERR_INVALID_ARG;
   if (c->init_scale != 0 && c->init_scale != 1) return AR_ERR_INVALID_ARG;
+  if (c->check_finite != 0 && c->check_finite != 1) return AR_ERR_INVALID_ARG;
   if (c->init_scale == 1) {
     int j0, j1;
     if (!finite(c->clip_lo) || !finite(c->clip_hi) || c->clip_lo <= 0.0f ||
@@ -372,6 +374,24 @@ ar_status check_step(const ar_config* c, const ar_state* s, const uint16_t* Xb, 
   return AR_OK;
 }
 
+// check_finite: AR_ERR_NONFINITE when any element of the given arrays is NaN or
+// infinite. Clears *dflag (device), scans on the stream, and waits for the
+// result on the host.
+struct ScanItem {
+  const void* p;
+  int64_t n;
+  int dt;
+};
+ar_status scan_finite(std::initializer_list<ScanItem> items, int* dflag, hipStream_t st) {
+  AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(dflag), 0.0f, 1, st));
+  for (const ScanItem& it : items) AR_TRY(ar_launch_nonfinite(it.p, it.n, it.dt, dflag, st));
+  int found = 0;
+  if (hipMemcpyAsync(&found, dflag, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return AR_ERR_HIP;
+  return found ? AR_ERR_NONFINITE : AR_OK;
+}
+
 // One SignSGD step of ar_tune_step on validated arguments, scratch at ws.
 // Everything the step reads from ws is written first by the same call (the
 // staged minibatch, Ŵ with its zero padding, the products, the loss
@@ -383,6 +403,12 @@ ar_status run_step(const ar_config* c, const ar_state* s, int g, const uint16_t*
   size_t need;
   StepWs w = carve_step(ws, N, K, Tb, ydt, &need);
   const BlkSizes z(N, K, Tb);
+  if (c->check_finite) {
+    const int64_t Gn = K / g;
+    AR_TRY(scan_finite({{s->W, N * K, s->wdt}, {s->V, N * K, AR_F32}, {s->alpha, N * Gn, AR_F32},
+                        {s->beta, N * Gn, AR_F32}, {Xb, Tb * K, AR_BF16}, {Yb, Tb * N, ydt}},
+                       w.flag + 1, st));
+  }
 
   // stage the minibatch into the blocked GEMM layouts, Ŵ of the current state
   AR_TRY(ar_launch_stage_x(Xb, w.XTB, w.XB, 1, Tb, K, z.nkbT, z.nkbK, st));
@@ -453,6 +479,7 @@ ar_status ar_config_default(ar_config* c) {
   c->clip_hi = 1.0f;
   c->init_scale = 0;
   c->mse_grid = 100;
+  c->check_finite = 0;
   return AR_OK;
 }
 
@@ -463,6 +490,7 @@ const char* ar_status_string(int32_t s) {
     case AR_ERR_UNSUPPORTED: return "unsupported (bits must be 2, 3, 4 or 8; group_size a multiple of 8; dtype f32/bf16)";
     case AR_ERR_SHAPE: return "shape constraint violated";
     case AR_ERR_WORKSPACE: return "workspace too small (ar_tune_step_noalloc: the problem needs more than its fixed scratch)";
+    case AR_ERR_NONFINITE: return "an input holds NaN or Inf (check_finite)";
     case AR_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
@@ -601,6 +629,8 @@ ar_status ar_tune_linear(const ar_config* c, int32_t wdt, const void* W, int64_t
     if (_s != AR_OK) return cleanup(_s); \
   } while (0)
 
+  if (c->check_finite)
+    AR_TRY_C(scan_finite({{W, N * K, wdt}, {X, M * K, AR_BF16}, {Y, M * N, ydt}}, w.flag + 1, st));
   // one-time staging of every minibatch into the blocked GEMM layouts
   AR_TRY_C(ar_launch_stage_x(X, w.XTB, w.XB, nb, Tb, K, z.nkbT, z.nkbK, st));
   AR_TRY_C(ar_launch_block_transpose(Y, w.YB, nb, Tb, N, z.nkbT, (int)ysz, st));
@@ -705,6 +735,10 @@ ar_status ar_tune_step_gram(const ar_config* c, const ar_state* s, const uint16_
   const GramSizes q(s->wdt, N, K, Tb);
   const BlkSizes z(N, K, Tb);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (c->check_finite)
+    AR_TRY(scan_finite({{s->W, N * K, s->wdt}, {s->V, N * K, AR_F32}, {s->alpha, N * Gn, AR_F32},
+                        {s->beta, N * Gn, AR_F32}, {Xb, Tb * K, AR_BF16}, {Yb, Tb * N, ydt}},
+                       w.flag + 1, st));
 
   AR_TRY(stage_gram_weight(w, q, s->wdt, s->W, N, K, st));
   AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(w.HB), 0.0f, q.hb / 2, st));
@@ -788,6 +822,8 @@ ar_status ar_tune_linear_gram(const ar_config* c, int32_t wdt, const void* W, in
     if (_s != AR_OK) return cleanup(_s); \
   } while (0)
 
+  if (c->check_finite)
+    AR_TRY_C(scan_finite({{W, N * K, wdt}, {X, M * K, AR_BF16}, {Y, M * N, ydt}}, w.flag + 1, st));
   // once per Linear: the statistics of every minibatch
   AR_TRY_C(stage_gram_weight(w, q, wdt, W, N, K, st));
   AR_TRY_C(ar_launch_fill_f32(reinterpret_cast<float*>(w.HB), 0.0f, nb * q.hb / 2, st));

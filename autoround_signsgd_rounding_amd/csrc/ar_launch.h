@@ -114,6 +114,9 @@ struct ArSteArgs {
 ar_status ar_launch_ste_update(const ArSteArgs& a, hipStream_t st);
 
 ar_status ar_launch_fill_f32(float* p, float v, int64_t n, hipStream_t st);
+// *flag = 1 when any of the n elements at p (dtype dt: AR_F32 or AR_BF16) is NaN
+// or infinite; *flag is not touched otherwise (the caller clears it first).
+ar_status ar_launch_nonfinite(const void* p, int64_t n, int dt, int* flag, hipStream_t st);
 
 // W-bit x bf16 product on the packed format (ar_dequant.hip). g % 8 == 0.
 // Dequantized bf16 Ŵ into the blocked operand (rows N, reduction K).

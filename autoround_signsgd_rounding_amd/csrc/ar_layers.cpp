@@ -94,8 +94,9 @@ ar_status ar_resolve_fused_config(const ar_layer_rule* rules, int32_t nrules,
                                   const ar_layer_qconfig* defaults, int32_t quantized,
                                   const char* layer_name, const char* const* sub_names,
                                   int32_t nsub, ar_layer_qconfig* out) {
+  // sub_names given with no entries is an empty sub-layer set: nothing to agree on
   if (!rules_ok(rules, nrules) || !defaults || !layer_name || !out || nsub < 0 ||
-      (nsub > 0 && !sub_names))
+      (nsub > 0) != (sub_names != nullptr))
     return AR_ERR_INVALID_ARG;
   try {
     const bool q = quantized != 0;

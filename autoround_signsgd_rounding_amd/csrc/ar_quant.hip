@@ -1,7 +1,7 @@
 // Quantizer-side kernels of the tuning step (gfx950): fake-quant, the
-// stand-alone straight-through fold + SignSGD update (for group sizes the
-// gradient product cannot fuse), staging of the GEMM operands into their
-// blocked layout, and int32 packing. All HBM-bound; every group of g
+// straight-through fold + SignSGD update that follows the gradient product,
+// staging of the GEMM operands into their blocked layout, and int32 packing.
+// All HBM-bound; every group of g
 // contiguous input channels of one output row is handled by LPG consecutive
 // lanes, each lane streaming 8-element chunks (16 B of bf16 / 32 B of float32)
 // so that a wave reads contiguous, coalesced spans.
@@ -172,8 +172,7 @@ __global__ __launch_bounds__(NT) void k_fakequant(FQArgs<WT, OT> a) {
 }
 
 // ONE: each lane holds exactly one chunk of its group (the whole step runs on
-// registers, shared with the gradient product's fused epilogue); otherwise
-// chunks are re-read per phase.
+// registers); otherwise chunks are re-read per phase.
 template <typename WT, int LPG, bool ONE>
 __global__ __launch_bounds__(NT) void k_ste_update(SteK<WT> a) {
   const int64_t gid = ((int64_t)blockIdx.x * NT + threadIdx.x) / LPG;
@@ -239,6 +238,37 @@ __global__ __launch_bounds__(NT) void k_ste_update(SteK<WT> a) {
 __global__ __launch_bounds__(NT) void k_fill_f32(float* p, float v, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT)
     p[i] = v;
+}
+
+// ------------------------------------------------------------------ non-finite scan
+// *flag = 1 when any of the nbytes / EB elements at p (float32: EB = 4, bf16:
+// EB = 2) is NaN or infinite (all exponent bits set); *flag is left as it is
+// otherwise. vec: p is 16-byte aligned and the bulk is read 16 bytes at a time.
+template <int EB>
+__device__ __forceinline__ bool word_nonfinite(uint32_t w) {
+  if (EB == 4) return (w & 0x7F800000u) == 0x7F800000u;
+  return (w & 0x7F80u) == 0x7F80u || (w & 0x7F800000u) == 0x7F800000u;
+}
+
+template <int EB>
+__global__ __launch_bounds__(NT) void k_nonfinite(const uint8_t* __restrict__ p, int64_t nbytes,
+                                                  int vec, int* flag) {
+  const int64_t tid = (int64_t)blockIdx.x * NT + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * NT;
+  const int64_t nvec = vec ? nbytes / 16 : 0;
+  bool bad = false;
+  const uint4* v = reinterpret_cast<const uint4*>(p);
+  for (int64_t i = tid; i < nvec; i += stride) {
+    const uint4 q = v[i];
+    bad |= word_nonfinite<EB>(q.x) | word_nonfinite<EB>(q.y) | word_nonfinite<EB>(q.z) |
+           word_nonfinite<EB>(q.w);
+  }
+  for (int64_t b = nvec * 16 + tid * EB; b < nbytes; b += stride * EB) {
+    const uint32_t w = EB == 4 ? *reinterpret_cast<const uint32_t*>(p + b)
+                               : (uint32_t)*reinterpret_cast<const uint16_t*>(p + b);
+    bad |= word_nonfinite<EB>(w);
+  }
+  if (bad) *flag = 1;
 }
 
 // ------------------------------------------------------------------ GEMM operand staging
@@ -691,6 +721,22 @@ ar_status ar_launch_fill_f32(float* p, float v, int64_t n, hipStream_t st) {
   const int64_t want = (n + NT - 1) / NT;
   const unsigned nb = (unsigned)(want < 65536 ? want : 65536);
   hipLaunchKernelGGL(k_fill_f32, dim3(nb), dim3(NT), 0, st, p, v, n);
+  return last_status();
+}
+
+ar_status ar_launch_nonfinite(const void* p, int64_t n, int dt, int* flag, hipStream_t st) {
+  if (n <= 0) return AR_OK;
+  const int eb = dt == AR_BF16 ? 2 : 4;
+  const int64_t nbytes = n * eb;
+  const int vec = (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+  const int64_t units = vec ? (nbytes + 15) / 16 : n;
+  int64_t nb = (units + NT - 1) / NT;
+  if (nb > 4096) nb = 4096;
+  const uint8_t* b = static_cast<const uint8_t*>(p);
+  if (eb == 2)
+    hipLaunchKernelGGL(k_nonfinite<2>, dim3((unsigned)nb), dim3(NT), 0, st, b, nbytes, vec, flag);
+  else
+    hipLaunchKernelGGL(k_nonfinite<4>, dim3((unsigned)nb), dim3(NT), 0, st, b, nbytes, vec, flag);
   return last_status();
 }
 

@@ -1,5 +1,6 @@
-// Straight-through fold and SignSGD update of one weight group, shared by the
-// stand-alone update kernel and the gradient product's fused epilogue.
+// Straight-through fold and SignSGD update of one weight group, used by the
+// update kernel that runs after the gradient product (k_ste_update) and by the
+// Gram form's update kernel.
 //
 // Per element (float32): t = W/s, c = rint(t + V) + zp, q = clamp(c, 0, maxq),
 // m = [0 <= c <= maxq]; the rounding is passed straight through, so

@@ -69,9 +69,11 @@ def _measured_traffic(workload):
 
 
 def _cpu_baseline(case, Yd, w, steps=8):
-    """The CPU oracle as it stands, timed on `steps` SignSGD steps of the same
-    workload (full 4096x4096 problem, Tb = 16384 tokens per step)."""
-    import torch
+    """The CPU oracle as it stands on the same workload. A launch-bound layer
+    (under 1 GFLOP per iteration) is timed on its whole tuning run
+    (oracle.tune_linear, all w.iters iterations, restore and quantization);
+    a larger one on `steps` SignSGD steps of the full problem, minibatch
+    i mod nb for step i as in the tuning loop."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -83,28 +85,39 @@ def _cpu_baseline(case, Yd, w, steps=8):
                    seqlen=w.seqlen, batch_samples=w.batch_samples, iters=w.iters, lr=w.lr,
                    minmax_lr=w.minmax_lr, minmax_shrink=w.minmax_shrink)
     Tb = w.Tb
+    nb = w.nsamples // w.batch_samples
+    host = {"host_cpus": os.cpu_count(), "affinity_cpus": _affinity(),
+            "blas_threads": int(threads), "cpu_model": _cpu_model(),
+            "host": platform.processor() or platform.machine()}
+    batches = []
+    for b in range(min(steps, nb) if w.flop_per_iter >= 1e9 else nb):
+        xb = synth.bf16_bits_to_f32(case.X_bits[b * Tb:(b + 1) * Tb])
+        yb = Yd[b * Tb:(b + 1) * Tb].float().cpu().numpy()
+        batches.append((xb, yb))
+    if w.flop_per_iter < 1e9:
+        t0 = time.perf_counter()
+        O.tune_linear(case.W, lambda b: batches[b], nb, cfg)
+        el = time.perf_counter() - t0
+        return {"value": w.iters / el, "unit": "iters/s", "cores": int(threads),
+                "kind": "oracle",
+                "sample": f"the whole {w.iters}-iteration tuning run of the {w.N}x{w.K} layer "
+                          f"(staging, every SignSGD step, best-state restore, final "
+                          f"quantization) in {el:.3f} s", **host}
     V = np.zeros((w.N, w.K), np.float32)
     wmin, wmax = O.group_minmax(case.W, w.group_size)
     a = np.full(wmin.shape, np.float32(w.minmax_shrink))
     b = a.copy()
-    batches = []
-    for i in range(steps):
-        xb = synth.bf16_bits_to_f32(case.X_bits[i * Tb:(i + 1) * Tb])
-        yb = Yd[i * Tb:(i + 1) * Tb].float().cpu().numpy()
-        batches.append((xb, yb))
     t0 = time.perf_counter()
     for i in range(steps):
-        r = O.tune_step(case.W, V, a, b, wmin, wmax, batches[i][0], batches[i][1], cfg)
+        xb, yb = batches[i % len(batches)]
+        r = O.tune_step(case.W, V, a, b, wmin, wmax, xb, yb, cfg)
         V, a, b = r.V, r.alpha, r.beta
     el = time.perf_counter() - t0
     return {"value": steps / el, "unit": "iters/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{steps} SignSGD steps (fwd+wgrad contractions, STE fold, update) of the "
                       f"full {w.N}x{w.K} problem on {Tb}-token minibatches; "
-                      f"{el / steps:.2f} s/step; a 200-iteration run extrapolates to "
-                      f"{200 * el / steps / 60:.1f} min",
-            "host_cpus": os.cpu_count(), "affinity_cpus": _affinity(),
-            "blas_threads": int(threads), "cpu_model": _cpu_model(),
-            "host": platform.processor() or platform.machine()}
+                      f"{el / steps:.2f} s/step; a {w.iters}-iteration run extrapolates to "
+                      f"{w.iters * el / steps / 60:.1f} min", **host}
 
 
 def _affinity():
@@ -356,6 +369,80 @@ def _block_run(ar, torch, iters=200):
             "block_out_mse": mse}
 
 
+def _graph_steps(ar, torch, W, X, Y, cfg, w, ws, args, step):
+    """Steps of a launch-bound layer: ar_tune_linear + ar_pack captured once in
+    a HIP graph (no allocation or memset inside: the buffers come from the
+    capture's pool, the library clears with fill kernels), one replay per
+    step. Every replay recomputes the whole job from the same inputs; the
+    last replay's outputs must equal an eager call's bit for bit. Per-kernel
+    times come from `args.steps` eager calls with HIP events around every
+    step's kernels. Returns (eager records, seconds for the timed replays,
+    check record)."""
+    recs = []
+    for _ in range(args.steps):
+        step(recs)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s2 = torch.cuda.Stream()
+    with torch.cuda.stream(s2):
+        with torch.cuda.graph(g, stream=s2):
+            gout = ar.tune_linear(W, X, Y, cfg, want_state=False, workspace=ws)
+            gqw, gqz = ar.pack(gout.codes, gout.zp, w.bits)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        g.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ref = recs[-1][1]
+    rqw, rqz = ar.pack(ref.codes, ref.zp, w.bits)
+    same = (torch.equal(gout.codes, ref.codes) and torch.equal(gout.scale, ref.scale)
+            and torch.equal(gout.zp, ref.zp) and torch.equal(gqw, rqw) and torch.equal(gqz, rqz)
+            and torch.equal(gout.losses, ref.losses))
+    if not same:
+        raise RuntimeError("graph replay differs from the eager call")
+    return recs, el, {"replays": args.warmup + args.steps, "equal_to_eager": same}
+
+
+def _yardstick(torch, w, reps=50):
+    """The vendor library's GEMM (torch -> hipBLASLt, run as a black box) on the
+    step's two contraction shapes, bf16 operands with float32 accumulation:
+    forward Y' = X_b·Ŵᵀ (F.linear, [Tb, K] x [N, K]) and gradient G = dYᵀ·X_b
+    (torch.mm on the transposed view, [Tb, N]ᵀ x [Tb, K]), on random operands.
+    HIP events around `reps` calls on the current stream, after 5 untimed."""
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    X = torch.randn((w.Tb, w.K), device=dev, generator=gen).to(torch.bfloat16)
+    W = (torch.randn((w.N, w.K), device=dev, generator=gen) * 0.02).to(torch.bfloat16)
+    dY = (torch.randn((w.Tb, w.N), device=dev, generator=gen) * 0.01).to(torch.bfloat16)
+    flop = 2.0 * w.Tb * w.K * w.N
+    calls = {"forward": lambda: torch.nn.functional.linear(X, W),
+             "gradient": lambda: torch.mm(dY.t(), X)}
+    out = {"workload": w.name, "shapes": {"forward": [w.Tb, w.K, w.N],
+                                          "gradient": [w.N, w.Tb, w.K]}}
+    stream = torch.cuda.current_stream()
+    for name, fn in calls.items():
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = flop / (ms * 1e-3) / 1e12
+        out[name] = {"us": round(ms * 1e3, 1), "TFLOP/s": round(tf, 1),
+                     "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return out
+
+
 def _gram_run(ar, torch, W, X, Y, cfg, w, args):
     """The same job in the Gram form (ar_tune_linear_gram + ar_pack): per-minibatch
     statistics staged inside the call, then one D·H product (2·N·K·3K FLOP on a
@@ -410,6 +497,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="llama7b_q_proj")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", choices=("auto", "on", "off"), default="auto",
+                    help="time steps as replays of one HIP graph holding the whole call "
+                         "(auto: for launch-bound layers under 1 GFLOP per iteration)")
     ap.add_argument("--no-gram", action="store_true",
                     help="skip the Gram-form run reported under detail.gram")
     ap.add_argument("--no-block", action="store_true",
@@ -421,6 +511,10 @@ def main():
                     help="only run the one-token packed-format product on the 29568x8192 W4 "
                          "layer at every bit width and print its record (for profiles of that "
                          "kernel alone)")
+    ap.add_argument("--yardstick", action="store_true",
+                    help="only time the black-box library GEMM (torch: hipBLASLt) on the two "
+                         "contraction shapes of the workload's step and print its record "
+                         "(for counter profiles of that GEMM beside the library's)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -446,6 +540,10 @@ def main():
     if args.block_only:
         print(json.dumps({"block": _block_run(ar, torch)}), flush=True)
         return
+    if args.yardstick:
+        print(json.dumps({"yardstick": _yardstick(torch, synth.WORKLOADS[args.workload])}),
+              flush=True)
+        return
     if args.dequant_only:
         print(json.dumps({"dequant_decode": [_decode_large(ar, torch, 20, bits=b)
                                              for b in (4, 2, 3, 8)]}), flush=True)
@@ -468,23 +566,26 @@ def main():
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
-    stream = torch.cuda.current_stream()
+    graph = args.graph == "on" or (args.graph == "auto" and w.flop_per_iter < 1e9)
 
     def step(times):
         out = ar.tune_linear(W, X, Y, cfg, want_state=False, timed=True,
-                             time_every=TIME_EVERY, workspace=ws)
+                             time_every=1 if graph else TIME_EVERY, workspace=ws)
         ar.pack(out.codes, out.zp, w.bits)
         times.append((out.times, out))
 
-    for _ in range(args.warmup):
-        step([])
-    torch.cuda.synchronize()
-    recs = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(recs)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
+    if graph:
+        recs, el, graph_check = _graph_steps(ar, torch, W, X, Y, cfg, w, ws, args, step)
+    else:
+        for _ in range(args.warmup):
+            step([])
+        torch.cuda.synchronize()
+        recs = []
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(recs)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
 
     iters_total = w.iters * args.steps
     value = iters_total / el
@@ -520,8 +621,9 @@ def main():
                         f"{'sym' if w.sym else 'asym'} g{w.group_size}, "
                         f"{w.nsamples}x{w.seqlen} calibration tokens, minibatch "
                         f"{w.batch_samples}x{w.seqlen}, {w.iters} iters, lr {w.lr}",
-            "step": "ar_tune_linear (200 SignSGD iterations incl. staging and final "
-                    "quantization) + ar_pack",
+            "step": f"ar_tune_linear ({w.iters} SignSGD iterations incl. staging and final "
+                    f"quantization) + ar_pack" + (", captured once in a HIP graph and replayed "
+                                                  "(one replay per step)" if graph else ""),
             "N": w.N, "K": w.K, "Tb": w.Tb, "M": w.M, "iters": w.iters,
         },
         "roofline": {
@@ -539,8 +641,10 @@ def main():
             "ms_per_iter": round(el / iters_total * 1e3, 4),
             "kernel_ms_per_iter": {"fwd_gemm": round(fwd_ms, 4), "wgrad_gemm": round(wgrad_ms, 4),
                                    "ste_update": round(ste_ms, 4)},
-            "kernel_timing": f"HIP events around the kernels of every {TIME_EVERY}th step "
-                             f"({timed_steps} steps timed)",
+            "kernel_timing": (f"HIP events around the kernels of every step of "
+                              f"{len(recs)} eager calls ({timed_steps} steps timed)" if graph else
+                              f"HIP events around the kernels of every {TIME_EVERY}th step "
+                              f"({timed_steps} steps timed)"),
             "fwd_gemm_tflops": round(gemm_flop / (fwd_ms * 1e-3) / 1e12, 1),
             "wgrad_gemm_tflops": round(gemm_flop / (wgrad_ms * 1e-3) / 1e12, 1),
             "pack_ms": round(pack_ms, 4),
@@ -552,9 +656,12 @@ def main():
             "input_gen_s": round(t_gen, 1),
         },
     }
+    if graph:
+        line["detail"]["graph_check"] = graph_check
     line["detail"]["tune_step"] = _step_run(ar, torch, W, X, Y, cfg, w)
-    line["detail"]["dequant_gemm"] = _dequant_run(ar, torch, X, recs[-1][1], w)
-    if not args.no_block:
+    if not graph:
+        line["detail"]["dequant_gemm"] = _dequant_run(ar, torch, X, recs[-1][1], w)
+    if not args.no_block and not graph:
         line["detail"]["block"] = _block_run(ar, torch)
     if not args.no_gram:
         line["detail"]["gram"] = _gram_run(ar, torch, W, X, Y, cfg, w, args)

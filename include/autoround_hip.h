@@ -48,6 +48,7 @@ typedef enum {
   AR_ERR_UNSUPPORTED = 2,   /* bits not in {2,3,4,8} (16 = "leave unquantized"), bad dtype */
   AR_ERR_SHAPE = 3,         /* size constraint violated */
   AR_ERR_WORKSPACE = 4,     /* ws_bytes smaller than the *_workspace_size result */
+  AR_ERR_NONFINITE = 5,     /* check_finite set and an input holds NaN or Inf */
   AR_ERR_HIP = 6            /* a HIP runtime call or kernel launch failed */
 } ar_status;
 
@@ -74,6 +75,19 @@ typedef struct {
                             squared weight errors (float32 errors, float64 sum, first
                             minimum on ties)                                              */
   int32_t mse_grid;      /* grid steps per unit shrink for init_scale = 1 (default 100)   */
+  int32_t check_finite;  /* 0 (default): no check. A NaN or Inf in the data then makes
+                            the loss of every step that reads it NaN: such a step is
+                            never taken as the best (the comparison is a strict <), and
+                            its non-finite gradients move nothing (sgn(NaN) = 0), so the
+                            returned state stays finite. The [LLMC] tuning loop reads
+                            each batch loss on the host; this loop does not.
+                            1: the tuning entry points (ar_tune_step, ar_tune_linear and
+                            their Gram and no-allocation forms) first scan their inputs
+                            (W, X, Y; the step also V, alpha, beta) on the device and
+                            return AR_ERR_NONFINITE, with no output written, when any
+                            element is NaN or infinite. The call then blocks until the
+                            scan's result is on the host, so it cannot be captured in a
+                            HIP graph. ar_tune_block passes it to each Linear's tuning. */
 } ar_config;
 
 /* Per-kernel device time of one ar_tune_linear call, measured with HIP events
@@ -327,9 +341,11 @@ ar_status ar_resolve_layer_config(const ar_layer_rule* rules, int32_t nrules,
                                   const char* name, ar_layer_qconfig* out);
 
 /* Config of a fused layer: every sub-layer must resolve to the same config,
-   else AR_ERR_INVALID_ARG. With nsub > 0 the sub-layers are sub_names (a fused
-   q/k/v-style layer). With nsub = 0 they are the rule keys that start with
-   layer_name (a fused expert layer); with no such key, layer_name itself. */
+   else AR_ERR_INVALID_ARG. With sub_names set (nsub > 0) the sub-layers are
+   sub_names (a fused q/k/v-style layer). With sub_names NULL (nsub = 0) they
+   are the rule keys that start with layer_name (a fused expert layer); with
+   no such key, layer_name itself. sub_names set with nsub = 0 (an empty
+   sub-layer list) is AR_ERR_INVALID_ARG, as is sub_names NULL with nsub > 0. */
 ar_status ar_resolve_fused_config(const ar_layer_rule* rules, int32_t nrules,
                                   const ar_layer_qconfig* defaults, int32_t quantized,
                                   const char* layer_name, const char* const* sub_names,

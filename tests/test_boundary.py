@@ -44,10 +44,21 @@ def test_config_default_and_strings():
         (4, 128, 0, 128, 2048, 8, 200)
     assert abs(c.lr - 0.005) < 1e-9 and c.minmax_lr < 0 and c.minmax_shrink == 1.0
     assert (c.clip_lo, c.clip_hi) == (0.5, 1.0)
-    assert (c.init_scale, c.mse_grid) == (0, 100)
+    assert (c.init_scale, c.mse_grid, c.check_finite) == (0, 100, 0)
     assert ar.lib.ar_config_default(None) == INV
-    for s in (0, 1, 2, 3, 4, 6, 99):
+    for s in (0, 1, 2, 3, 4, 5, 6, 99):
         assert len(ar.lib.ar_status_string(s)) > 0
+    assert b"NaN" in ar.lib.ar_status_string(5)
+    assert ar.STATUS[5] == "AR_ERR_NONFINITE"
+
+
+def test_check_finite_flag_validation():
+    """check_finite is 0 or 1; any other value is refused before any HIP call."""
+    c, cc = cfg()
+    cc.check_finite = 2
+    assert rtn(ctypes.byref(cc)) == INV
+    cc.check_finite = 1
+    assert rtn(ctypes.byref(cc), N=0) == OK
 
 
 def rtn(c, wdt=1, W=P, N=8, K=128, Wq=NULL, codes=NULL):

@@ -43,7 +43,9 @@ def test_hand_vectors_on_gpu():
             torch.from_numpy(a).to(dev()), torch.from_numpy(b).to(dev()), cfg)
         np.testing.assert_array_equal(to_np(codes)[0, :4], c["codes"])
         assert to_np(scale)[0, 0] == F32(c["s"]) and to_np(zp)[0, 0] == c["zp"]
-        np.testing.assert_array_equal(to_np(Wq)[0, :4], np.array(c["what"], F32))
+        # Wq is the bf16 operand: the hand value rounded to bf16 (a library cast)
+        want = torch.tensor(c["what"], dtype=torch.float32).to(torch.bfloat16).float().numpy()
+        np.testing.assert_array_equal(to_np(Wq)[0, :4], want)
         oc, os_, oz, ow = _oracle_fq(W, V, a, b, oracle_cfg(cfg))
         np.testing.assert_array_equal(to_np(codes), oc)
         np.testing.assert_array_equal(to_np(scale).view(np.uint32), os_.view(np.uint32))

@@ -77,6 +77,20 @@ def test_fused_layers():
         ar.resolve_fused_config(bad, DEF, True, "e.experts")
 
 
+def test_fused_layer_with_empty_sub_layer_list():
+    """An explicit empty sub-layer list has no config to agree on: both sides
+    reject it ([SGLang] "4. FusedMoE와 Fused QKV 처리" requires one config
+    shared by the sub-layers), while no list at all (None) is the fused-expert
+    rule, which collects the sub-layers from the rule keys."""
+    rules = [("experts.0", {"bits": 8}), ("experts.1", {"bits": 8})]
+    with pytest.raises(ValueError):
+        O.resolve_fused_config(rules, DEF, True, "experts", [])
+    with pytest.raises(ar.ArError):
+        ar.resolve_fused_config(rules, DEF, True, "experts", [])
+    assert ar.resolve_fused_config(rules, DEF, True, "experts") == \
+        tuple(O.resolve_fused_config(rules, DEF, True, "experts")) == (8, 128, False)
+
+
 def test_null_arguments():
     import ctypes
     out = ar.ArLayerQConfig()
