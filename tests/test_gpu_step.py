@@ -146,7 +146,7 @@ def test_tune_step_full_size(name):
     """One step at the workload's full shape and minibatch (Tb = 16384 tokens),
     launched as the tuning loop launches it. Rows of the problem are independent
     apart from the loss normalisation, so the oracle checks the gradients and
-    updated state of 32 sampled rows; the loss is checked in full for q_proj."""
+    updated state of 32 sampled rows, and the loss of the whole problem."""
     w = synth.WORKLOADS[name]
     log(f"tune_step full size {name}")
     case = synth.make_case(w.N, w.K, w.Tb, wdtype=w.wdtype, sigma_w=w.sigma_w,
@@ -175,10 +175,56 @@ def test_tune_step_full_size(name):
     agree = np.mean(to_np(Vd[rt]) == r.V)
     log(f"  sampled rows: updated V agree {agree:.6f}")
     assert agree >= 0.999
-    if name == "llama7b_q_proj":
-        wmin, wmax = O.group_minmax(case.W, w.group_size)
-        qp = O.qparams(wmin, wmax, a, b, w.bits, w.sym)
-        fq = O.fake_quant(case.W, V, qp, w.bits, w.group_size)
-        Lo, _, _ = O.forward_backward(Xf, to_np(Yd), fq.what)
-        log(f"  oracle loss {Lo:.6e}")
-        assert abs(L - Lo) <= TOL * Lo
+    Lo = _oracle_loss(case.W, V, a, b, Xf, to_np(Yd), w.group_size, w.bits, w.sym)
+    log(f"  oracle loss {Lo:.6e}")
+    assert abs(L - Lo) <= TOL * Lo
+
+
+def _oracle_loss(W, V, a, b, Xf, Y, g, bits, sym, chunk=4096):
+    """The oracle's loss of the whole problem, summed over row chunks (rows are
+    independent apart from the normalisation, which n_scale carries)."""
+    N = W.shape[0]
+    total = 0.0
+    for r0 in range(0, N, chunk):
+        sl = slice(r0, min(N, r0 + chunk))
+        wmin, wmax = O.group_minmax(W[sl], g)
+        qp = O.qparams(wmin, wmax, a[sl], b[sl], bits, sym)
+        fq = O.fake_quant(W[sl], V[sl], qp, bits, g)
+        _, _, ls = O.forward_backward(Xf, Y[:, sl], fq.what, n_scale=N)
+        total += ls
+    return total / (Xf.shape[0] * N)
+
+
+def test_tune_step_partial_last_wave():
+    """A shape whose products have a partial last wave (17 x 17 = 289 gradient
+    tiles and 8 x 17 forward tiles for 256 compute units): the loss of the
+    whole problem, the gradients and updated state of 64 sampled rows (every
+    tile column), and two runs bit for bit."""
+    N = K = 4352
+    Tb = 2048
+    log(f"tune_step partial last wave N={N} K={K} Tb={Tb}")
+    case, Yf, Yd = _inputs(N, K, Tb, "bf16", "bf16", seed=21)
+    G = K // 128
+    V, a, b = _state(N, K, G, seed=22)
+    cfg = ar.Config(bits=4, group_size=128)
+    outs = []
+    for _ in range(2):
+        Vd, ad, bd = _gpu(V, a, b)
+        loss, gV, ga, gb = ar.tune_step(weight_dev(case), Vd, ad, bd, bf16_dev(case.X_bits), Yd,
+                                        cfg)
+        torch.cuda.synchronize()
+        outs.append([to_np(t) for t in (loss, gV, ga, gb, Vd, ad, bd)])
+    for x, y in zip(*outs):
+        np.testing.assert_array_equal(x.view(np.uint32), y.view(np.uint32))
+    L, gV, ga, gb, Vn = outs[0][0][0], outs[0][1], outs[0][2], outs[0][3], outs[0][4]
+    rows = np.sort(np.random.default_rng(2).choice(N, 64, replace=False))
+    Xf = synth.bf16_bits_to_f32(case.X_bits)
+    wmin, wmax = O.group_minmax(case.W[rows], 128)
+    r = O.tune_step(case.W[rows], V[rows], a[rows], b[rows], wmin, wmax, Xf, Yf[:, rows],
+                    oracle_cfg(cfg), n_scale=N)
+    assert rel_norm(gV[rows], r.gV) <= TOL
+    assert rel_norm(ga[rows], r.galpha) <= TOL and rel_norm(gb[rows], r.gbeta) <= TOL
+    assert np.mean(Vn[rows] == r.V) >= 0.999
+    Lo = _oracle_loss(case.W, V, a, b, Xf, Yf, 128, 4, False)
+    log(f"  loss {L:.6e} vs oracle {Lo:.6e}")
+    assert abs(L - Lo) <= TOL * Lo
