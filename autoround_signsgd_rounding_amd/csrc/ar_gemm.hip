@@ -699,9 +699,185 @@ struct EpiWgrad {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Small products (at most SMALL_MAX_TILES tiles of 256 x 256): the large kernels
+// would run them on one or a few workgroups, which is what a toy layer's step
+// costs. Here each wave owns a 64 x 64 tile (2 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16), four waves per workgroup (2 x 2 tiles, 128 x 128),
+// and loads its fragments from the blocked operands straight into registers,
+// SM_D steps ahead (the fragment layout is the one the LDS reads of the large
+// kernels use); the forward's targets are loaded before the main loop. A
+// product this small is bound by memory latency, so the kernel spends
+// registers (one wave per SIMD) to keep the round trips few. Every output element gets the same sequence of MFMAs as in the
+// large kernels (per 32-wide step, substep 0 then substep 1), so G and dY come
+// out the same; only the forward's sums of R² are grouped per 64 x 64 tile.
+constexpr int SMALL_MAX_TILES = 4;
+constexpr int SM_D = 8;   // steps of fragments in flight
+
+enum { SM_FWD_F32 = 0, SM_FWD_BF16 = 1, SM_WGRAD = 2 };
+
+struct SmallArgs {
+  const uint16_t* P;   // rows rowsP (forward: X_b, gradient: dYᵀ), nkb blocks per panel
+  const uint16_t* Q;   // rows rowsQ (forward: Ŵ, gradient: X_bᵀ)
+  int nkb;
+  int tQ;              // 128-row workgroup tiles along Q
+  // forward: targets and dYᵀ blocked (rows n, reduction t, nkbT blocks)
+  const void* yB;
+  uint16_t* dyB;
+  float* partials;     // one per 64 x 64 tile: (2 * tile row) * (2 * tQ) + tile column
+  int nkbT;
+  // gradient: G [N, K] row-major, scaled; the previous forward's loss in workgroup 0
+  float* G;
+  int64_t N, K;
+  float scale;
+  ArLossIn loss;
+};
+
+template <int MODE>
+__global__ __launch_bounds__(NTHR) void k_gemm_small(SmallArgs a) {
+  __shared__ double sh[256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (MODE == SM_WGRAD && blockIdx.x == 0 && a.loss.partials) loss_reduce_block(a.loss, sh);
+  const int wgP = (int)blockIdx.x / a.tQ, wgQ = (int)blockIdx.x - wgP * a.tQ;
+  const int64_t r0 = (int64_t)wgP * 128 + (wave >> 1) * 64;   // the wave's rows of P
+  const int64_t c0 = (int64_t)wgQ * 128 + (wave & 1) * 64;    // and of Q
+  const int nk = a.nkb;
+  const uint16_t* pb = a.P + (r0 >> 8) * (int64_t)nk * arblk::BLOCK_ELEMS;
+  const uint16_t* qb = a.Q + (c0 >> 8) * (int64_t)nk * arblk::BLOCK_ELEMS;
+  // fragment (b, ks): row (r0 & 255) + 32b + (lane & 31) of a block, logical chunk
+  // 2 ks + (lane >> 5), stored at chunk ^ ((row >> 2) & 3) (ar_blocked.h)
+  const int sw = ((lane & 31) >> 2) & 3;
+  uint32_t oP[2][2], oQ[2][2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t ch = (uint32_t)(((2 * ks + (lane >> 5)) ^ sw) << 3);
+      oP[b][ks] = (uint32_t)((r0 & 255) + 32 * b + (lane & 31)) * BK + ch;
+      oQ[b][ks] = (uint32_t)((c0 & 255) + 32 * b + (lane & 31)) * BK + ch;
+    }
+  bf16x8_t fa[SM_D][2][2], fb[SM_D][2][2];
+  auto load = [&](int s, int u) {
+    const uint16_t* P = pb + (int64_t)s * arblk::BLOCK_ELEMS;
+    const uint16_t* Q = qb + (int64_t)s * arblk::BLOCK_ELEMS;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        fa[u][b][ks] = *reinterpret_cast<const bf16x8_t*>(P + oP[b][ks]);
+        fb[u][b][ks] = *reinterpret_cast<const bf16x8_t*>(Q + oQ[b][ks]);
+      }
+  };
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
+#pragma unroll
+  for (int u = 0; u < SM_D; ++u)
+    if (u < nk) load(u, u);
+  // forward: the targets of the lane's accumulator elements (4 tokens each, at
+  // element offset toff[bj][bi][q] of the blocked arrays), loaded up front
+  uint32_t toff[2][2][4];
+  f32x4_t yv[2][2][4];
+  if constexpr (MODE != SM_WGRAD) {
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n = c0 + bj * 32 + (lane & 31);
+          const int64_t t = r0 + bi * 32 + q * 8 + (lane >> 5) * 4;
+          const uint32_t off = (uint32_t)arblk::offset(n, t, a.nkbT);
+          toff[bj][bi][q] = off;
+          if constexpr (MODE == SM_FWD_F32) {
+            yv[bj][bi][q] = *reinterpret_cast<const f32x4_t*>(static_cast<const float*>(a.yB) + off);
+          } else {
+            const u32x2_t v = *reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(a.yB) + off);
+            yv[bj][bi][q] = f32x4_t{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u),
+                                    __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xFFFF0000u)};
+          }
+        }
+  }
+  for (int s0 = 0; s0 < nk; s0 += SM_D) {
+#pragma unroll
+    for (int u = 0; u < SM_D; ++u) {
+      const int s = s0 + u;
+      if (s < nk) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+              acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[u][bi][ks], fb[u][bj][ks],
+                                                                    acc[bi][bj], 0, 0, 0);
+        if (s + SM_D < nk) load(s + SM_D, u);
+      }
+    }
+  }
+
+  // accumulator element (bi, bj, e): row r0 + bi*32 + 8*(e >> 2) + 4*(lane >> 5) + (e & 3)
+  // of P, row c0 + bj*32 + (lane & 31) of Q
+  if constexpr (MODE == SM_WGRAD) {
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+      const int64_t k = c0 + bj * 32 + (lane & 31);
+      if (k < a.K) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t n = r0 + bi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            if (n < a.N) a.G[n * a.K + k] = acc[bi][bj][e] * a.scale;
+          }
+      }
+    }
+  } else {
+    // R = Y' - Y_true, dYᵀ = bf16(R) (padding rows and columns give R = 0)
+    float sq = 0.0f;
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float r[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            r[e] = acc[bi][bj][q * 4 + e] - yv[bj][bi][q][e];
+            sq += r[e] * r[e];
+          }
+          u32x2_t o;
+          o[0] = bf16_bits(r[0]) | (bf16_bits(r[1]) << 16);
+          o[1] = bf16_bits(r[2]) | (bf16_bits(r[3]) << 16);
+          *reinterpret_cast<u32x2_t*>(a.dyB + toff[bj][bi][q]) = o;
+        }
+    sq = wave_sum64(sq);
+    if (lane == 0)
+      a.partials[(2 * wgP + (wave >> 1)) * (2 * a.tQ) + 2 * wgQ + (wave & 1)] = sq;
+  }
+}
+
+bool small_product(int64_t rowsP, int64_t rowsQ) {
+  return arblk::row_tiles(rowsP) * arblk::row_tiles(rowsQ) <= SMALL_MAX_TILES;
+}
+int64_t tiles128(int64_t R) { return (R + 127) / 128; }
+// The forward covers whole 256-row panels, padding included, as the 256 x 256
+// kernels do: the gradient product reduces over every token of the padded
+// panels, so every dYᵀ element there must be written (R = 0 in padding).
+int64_t fwd_tiles128(int64_t R) { return 2 * arblk::row_tiles(R); }
+
 }  // namespace
 
-int ar_fwd_tiles(int64_t Tb, int64_t N) { return (int)(arblk::row_tiles(Tb) * arblk::row_tiles(N)); }
+int ar_fwd_tiles(int64_t Tb, int64_t N) {
+  if (small_product(Tb, N)) return (int)(4 * fwd_tiles128(Tb) * fwd_tiles128(N));
+  return (int)(arblk::row_tiles(Tb) * arblk::row_tiles(N));
+}
 
 ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void* yB, int ydt,
                              uint16_t* dyB, float* partials, int64_t Tb, int64_t N, int64_t K,
@@ -713,7 +889,16 @@ ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void*
   a.tilesJ = (int)arblk::row_tiles(N);
   const int nkbT = (int)(arblk::row_tiles(Tb) * (BM / BK));
   const int nwg = a.tilesI * a.tilesJ;
-  if (ydt == AR_BF16 && a.nkb >= FS_MIN_NK) {
+  if (small_product(Tb, N)) {
+    SmallArgs s{};
+    s.P = XB; s.Q = WB; s.nkb = a.nkb; s.tQ = (int)fwd_tiles128(N);
+    s.yB = yB; s.dyB = dyB; s.partials = partials; s.nkbT = nkbT;
+    const dim3 grid((unsigned)(fwd_tiles128(Tb) * fwd_tiles128(N)));
+    if (ydt == AR_BF16)
+      hipLaunchKernelGGL(k_gemm_small<SM_FWD_BF16>, grid, dim3(NTHR), 0, st, s);
+    else
+      hipLaunchKernelGGL(k_gemm_small<SM_FWD_F32>, grid, dim3(NTHR), 0, st, s);
+  } else if (ydt == AR_BF16 && a.nkb >= FS_MIN_NK) {
     FwdStreamArgs s{XB, WB, static_cast<const uint16_t*>(yB), dyB, partials,
                     a.nkb, a.tilesI, a.tilesJ, nkbT, nwg};
     hipLaunchKernelGGL(k_fwd_stream, dim3(fwd_stream_grid(nwg)), dim3(NTHR), 0, st, s);
@@ -814,6 +999,13 @@ ar_status ar_launch_gemm_gram(const uint16_t* DB, const uint16_t* HB, float* P, 
 ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* G, int64_t N,
                                int64_t K, int64_t Tb, float scale, const ArLossIn& loss,
                                hipStream_t st) {
-  return ar_launch_gemm_f32out(dyB, XTB, G, N, K, arblk::row_tiles(Tb) * (BM / BK), scale, loss,
-                               st);
+  const int64_t nkb = arblk::row_tiles(Tb) * (BM / BK);
+  if (!small_product(N, K))
+    return ar_launch_gemm_f32out(dyB, XTB, G, N, K, nkb, scale, loss, st);
+  SmallArgs s{};
+  s.P = dyB; s.Q = XTB; s.nkb = (int)nkb; s.tQ = (int)tiles128(K);
+  s.G = G; s.N = N; s.K = K; s.scale = scale; s.loss = loss;
+  hipLaunchKernelGGL(k_gemm_small<SM_WGRAD>, dim3((unsigned)(tiles128(N) * tiles128(K))),
+                     dim3(NTHR), 0, st, s);
+  return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }
