@@ -702,17 +702,21 @@ struct EpiWgrad {
 // ---------------------------------------------------------------------------
 // Small products (at most SMALL_MAX_TILES tiles of 256 x 256): the large kernels
 // would run them on one or a few workgroups, which is what a toy layer's step
-// costs. Here each wave owns a 64 x 64 tile (2 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16), four waves per workgroup (2 x 2 tiles, 128 x 128),
-// and loads its fragments from the blocked operands straight into registers,
-// SM_D steps ahead (the fragment layout is the one the LDS reads of the large
-// kernels use); the forward's targets are loaded before the main loop. A
-// product this small is bound by memory latency, so the kernel spends
-// registers (one wave per SIMD) to keep the round trips few. Every output element gets the same sequence of MFMAs as in the
+// costs. Here each workgroup is one wave that owns a 64 x 64 tile (2 x 2 blocks
+// of v_mfma_f32_32x32x16_bf16), so a product's operand loads spread over as
+// many CUs as it has such tiles. The wave loads its fragments from the blocked
+// operands straight into registers, SM_D steps ahead (the fragment layout is
+// the one the LDS reads of the large kernels use); the forward's targets are
+// loaded before the main loop. A product this small is bound by memory latency
+// and per-CU load bandwidth, so the kernel spends registers to keep the round
+// trips few. Every output element gets the same sequence of MFMAs as in the
 // large kernels (per 32-wide step, substep 0 then substep 1), so G and dY come
 // out the same; only the forward's sums of R² are grouped per 64 x 64 tile.
+// The gradient product's launch has one workgroup more, which reduces the
+// previous forward's loss while the others run.
 constexpr int SMALL_MAX_TILES = 4;
 constexpr int SM_D = 8;   // steps of fragments in flight
+constexpr int SM_THR = 64;
 
 enum { SM_FWD_F32 = 0, SM_FWD_BF16 = 1, SM_WGRAD = 2 };
 
@@ -720,11 +724,11 @@ struct SmallArgs {
   const uint16_t* P;   // rows rowsP (forward: X_b, gradient: dYᵀ), nkb blocks per panel
   const uint16_t* Q;   // rows rowsQ (forward: Ŵ, gradient: X_bᵀ)
   int nkb;
-  int tQ;              // 128-row workgroup tiles along Q
+  int nQ;              // 64 x 64 tiles along Q (tile t: row t / nQ, column t % nQ)
   // forward: targets and dYᵀ blocked (rows n, reduction t, nkbT blocks)
   const void* yB;
   uint16_t* dyB;
-  float* partials;     // one per 64 x 64 tile: (2 * tile row) * (2 * tQ) + tile column
+  float* partials;     // one per 64 x 64 tile, at its tile index
   int nkbT;
   // gradient: G [N, K] row-major, scaled; the previous forward's loss in workgroup 0
   float* G;
@@ -734,14 +738,15 @@ struct SmallArgs {
 };
 
 template <int MODE>
-__global__ __launch_bounds__(NTHR) void k_gemm_small(SmallArgs a) {
-  __shared__ double sh[256];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (MODE == SM_WGRAD && blockIdx.x == 0 && a.loss.partials) loss_reduce_block(a.loss, sh);
-  const int wgP = (int)blockIdx.x / a.tQ, wgQ = (int)blockIdx.x - wgP * a.tQ;
-  const int64_t r0 = (int64_t)wgP * 128 + (wave >> 1) * 64;   // the wave's rows of P
-  const int64_t c0 = (int64_t)wgQ * 128 + (wave & 1) * 64;    // and of Q
+__global__ __launch_bounds__(SM_THR) void k_gemm_small(SmallArgs a) {
+  const int lane = threadIdx.x;
+  if (MODE == SM_WGRAD && blockIdx.x == gridDim.x - 1) {   // the extra workgroup
+    if (a.loss.partials) loss_reduce_wave(a.loss);
+    return;
+  }
+  const int tP = (int)blockIdx.x / a.nQ, tQ = (int)blockIdx.x - tP * a.nQ;
+  const int64_t r0 = (int64_t)tP * 64;   // the wave's rows of P
+  const int64_t c0 = (int64_t)tQ * 64;   // and of Q
   const int nk = a.nkb;
   const uint16_t* pb = a.P + (r0 >> 8) * (int64_t)nk * arblk::BLOCK_ELEMS;
   const uint16_t* qb = a.Q + (c0 >> 8) * (int64_t)nk * arblk::BLOCK_ELEMS;
@@ -858,24 +863,23 @@ __global__ __launch_bounds__(NTHR) void k_gemm_small(SmallArgs a) {
           *reinterpret_cast<u32x2_t*>(a.dyB + toff[bj][bi][q]) = o;
         }
     sq = wave_sum64(sq);
-    if (lane == 0)
-      a.partials[(2 * wgP + (wave >> 1)) * (2 * a.tQ) + 2 * wgQ + (wave & 1)] = sq;
+    if (lane == 0) a.partials[blockIdx.x] = sq;
   }
 }
 
 bool small_product(int64_t rowsP, int64_t rowsQ) {
   return arblk::row_tiles(rowsP) * arblk::row_tiles(rowsQ) <= SMALL_MAX_TILES;
 }
-int64_t tiles128(int64_t R) { return (R + 127) / 128; }
+int64_t tiles64(int64_t R) { return (R + 63) / 64; }
 // The forward covers whole 256-row panels, padding included, as the 256 x 256
 // kernels do: the gradient product reduces over every token of the padded
 // panels, so every dYᵀ element there must be written (R = 0 in padding).
-int64_t fwd_tiles128(int64_t R) { return 2 * arblk::row_tiles(R); }
+int64_t fwd_tiles64(int64_t R) { return 4 * arblk::row_tiles(R); }
 
 }  // namespace
 
 int ar_fwd_tiles(int64_t Tb, int64_t N) {
-  if (small_product(Tb, N)) return (int)(4 * fwd_tiles128(Tb) * fwd_tiles128(N));
+  if (small_product(Tb, N)) return (int)(fwd_tiles64(Tb) * fwd_tiles64(N));
   return (int)(arblk::row_tiles(Tb) * arblk::row_tiles(N));
 }
 
@@ -891,13 +895,13 @@ ar_status ar_launch_gemm_fwd(const uint16_t* XB, const uint16_t* WB, const void*
   const int nwg = a.tilesI * a.tilesJ;
   if (small_product(Tb, N)) {
     SmallArgs s{};
-    s.P = XB; s.Q = WB; s.nkb = a.nkb; s.tQ = (int)fwd_tiles128(N);
+    s.P = XB; s.Q = WB; s.nkb = a.nkb; s.nQ = (int)fwd_tiles64(N);
     s.yB = yB; s.dyB = dyB; s.partials = partials; s.nkbT = nkbT;
-    const dim3 grid((unsigned)(fwd_tiles128(Tb) * fwd_tiles128(N)));
+    const dim3 grid((unsigned)(fwd_tiles64(Tb) * fwd_tiles64(N)));
     if (ydt == AR_BF16)
-      hipLaunchKernelGGL(k_gemm_small<SM_FWD_BF16>, grid, dim3(NTHR), 0, st, s);
+      hipLaunchKernelGGL(k_gemm_small<SM_FWD_BF16>, grid, dim3(SM_THR), 0, st, s);
     else
-      hipLaunchKernelGGL(k_gemm_small<SM_FWD_F32>, grid, dim3(NTHR), 0, st, s);
+      hipLaunchKernelGGL(k_gemm_small<SM_FWD_F32>, grid, dim3(SM_THR), 0, st, s);
   } else if (ydt == AR_BF16 && a.nkb >= FS_MIN_NK) {
     FwdStreamArgs s{XB, WB, static_cast<const uint16_t*>(yB), dyB, partials,
                     a.nkb, a.tilesI, a.tilesJ, nkbT, nwg};
@@ -1003,9 +1007,10 @@ ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* 
   if (!small_product(N, K))
     return ar_launch_gemm_f32out(dyB, XTB, G, N, K, nkb, scale, loss, st);
   SmallArgs s{};
-  s.P = dyB; s.Q = XTB; s.nkb = (int)nkb; s.tQ = (int)tiles128(K);
+  s.P = dyB; s.Q = XTB; s.nkb = (int)nkb; s.nQ = (int)tiles64(K);
   s.G = G; s.N = N; s.K = K; s.scale = scale; s.loss = loss;
-  hipLaunchKernelGGL(k_gemm_small<SM_WGRAD>, dim3((unsigned)(tiles128(N) * tiles128(K))),
-                     dim3(NTHR), 0, st, s);
+  // one workgroup per 64 x 64 tile of G, then the loss workgroup
+  hipLaunchKernelGGL(k_gemm_small<SM_WGRAD>, dim3((unsigned)(tiles64(N) * tiles64(K) + 1)),
+                     dim3(SM_THR), 0, st, s);
   return hipGetLastError() == hipSuccess ? AR_OK : AR_ERR_HIP;
 }

@@ -100,7 +100,7 @@ struct ArSteArgs {
   int g;
   ArGrid gr;
   float lr, mlr, clip_lo, clip_hi;
-  const int* flag;       // device: 1 = snapshot the current state
+  const int* flag;       // device, not null: 1 = snapshot the current state
   float* bestV;
   float* bestA;
   float* bestB;

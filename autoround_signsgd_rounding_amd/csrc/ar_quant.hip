@@ -181,15 +181,21 @@ __global__ __launch_bounds__(NT) void k_ste_update(SteK<WT> a) {
   const int64_t n = gid / a.Gn;
   const int64_t base = n * a.K + (gid - n * a.Gn) * a.g;
   const int64_t off0 = base + 8 * lig;
-  const bool snap = a.flag != nullptr && *a.flag != 0;
   if (ONE) {
+    // the chunk, the clip factors and the snapshot flag are all requested
+    // before the first wait: one round trip to memory for a small layer (the
+    // flag as a vector load, which the compiler keeps where it stands)
     float w[8], v[8], g[8];
     load8(a.W + off0, w);
     load8(a.V + off0, v);
     load8(a.G + off0, g);
-    ste_one<WT, LPG>(a, snap, gid, n, off0, lig, w, v, g, true);
+    const float al = a.alpha[gid], be = a.beta[gid];
+    const bool snap =
+        __hip_atomic_load(a.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+    ste_one<WT, LPG>(a, snap, gid, n, off0, lig, w, v, g, al, be, true);
     return;
   }
+  const bool snap = *a.flag != 0;
   const Grid gr = grid_of(a.gr);
 
   // phase 1: group min / max (the Min-Max range)
@@ -712,6 +718,7 @@ ar_status ar_launch_stage_x(const uint16_t* X, uint16_t* XTB, uint16_t* XB, int6
 }
 
 ar_status ar_launch_ste_update(const ArSteArgs& s, hipStream_t st) {
+  if (s.flag == nullptr) return AR_ERR_INVALID_ARG;
   return s.wdt == AR_BF16 ? ste_make<uint16_t>(s, st) : ste_make<float>(s, st);
 }
 

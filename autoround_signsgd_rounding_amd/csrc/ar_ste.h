@@ -157,13 +157,14 @@ __device__ __forceinline__ void clip_update(const SteK<WT>& a, bool snap, int64_
 }
 
 // One step for a group whose LPG lanes hold one 8-element chunk each (w, v, g
-// in registers; off = element offset of the chunk in [N, K], row n). Lanes of a
-// group with live = false (padding outside the matrix) take part in the group
-// reductions but touch no memory.
+// in registers; off = element offset of the chunk in [N, K], row n; al, be the
+// group's clip factors). Lanes of a group with live = false (padding outside
+// the matrix) take part in the group reductions but touch no memory.
 template <typename WT, int LPG>
 __device__ __forceinline__ void ste_one(const SteK<WT>& a, bool snap, int64_t gid, int64_t n,
                                         int64_t off, int lig, const float (&w)[8],
-                                        const float (&v)[8], const float (&g)[8], bool live) {
+                                        const float (&v)[8], const float (&g)[8], float al,
+                                        float be, bool live) {
   const Grid gr = grid_of(a.gr);
   float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
@@ -173,7 +174,7 @@ __device__ __forceinline__ void ste_one(const SteK<WT>& a, bool snap, int64_t gi
   }
   mn = group_min<LPG>(mn);
   mx = group_max<LPG>(mx);
-  const float al = live ? a.alpha[gid] : 1.0f, be = live ? a.beta[gid] : 1.0f;
+  if (!live) al = be = 1.0f;
   const QP p = group_qparams(mn, mx, al, be, gr);
   float A = 0.0f, Bs = 0.0f;
   ste_accum(w, v, g, p, gr, A, Bs);
