@@ -17,8 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libautoround_hip.so")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["ar_api.hip", "ar_gemm.hip", "ar_gram.hip", "ar_quant.hip", "ar_dequant.hip",
-           "ar_block.hip", "ar_layers.cpp"]
+SOURCES = ["ar_api.hip", "ar_gemm.hip", "ar_gemm_small.hip", "ar_gram.hip", "ar_quant.hip",
+           "ar_dequant.hip", "ar_block.hip", "ar_layers.cpp"]
 
 # -ffp-contract=off: the quantizer's float32 steps must round exactly as
 # written (no fused multiply-adds). Packed-fp32 instructions are disabled.
@@ -32,7 +32,7 @@ FLAGS = [
 # Kernels whose speed depends on running without register spills: the MFMA
 # contractions sit at the register file's limit. A spill (to scratch memory,
 # behind a full vector-memory wait) is reported as a warning.
-HOT = ("k_fwd_stream", "k_gemm", "k_dq_mfma", "k_attention")
+HOT = ("k_fwd_stream", "k_gemm", "k_gemm_small", "k_dq_mfma", "k_attention")
 _FN = re.compile(r"Function Name: (\S+)")
 _SPILL = re.compile(r"VGPRs Spill: (\d+)")
 

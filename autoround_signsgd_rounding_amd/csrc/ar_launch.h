@@ -51,7 +51,7 @@ struct ArLossIn {
 };
 // out[rowsP, rowsQ] (row-major float32) = scale * P·Qᵀ over nkb reduction
 // blocks (P rows rowsP, Q rows rowsQ, both blocked with nkb blocks per row
-// tile). Workgroup 0 reduces `loss` while its first stages load.
+// tile). `loss` (the previous forward's) is reduced in the same launch.
 ar_status ar_launch_gemm_f32out(const uint16_t* P, const uint16_t* Q, float* out, int64_t rowsP,
                                 int64_t rowsQ, int64_t nkb, float scale, const ArLossIn& loss,
                                 hipStream_t st);
@@ -63,6 +63,20 @@ ar_status ar_launch_gemm_gram(const uint16_t* DB, const uint16_t* HB, float* P, 
 ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* G, int64_t N,
                                int64_t K, int64_t Tb, float scale, const ArLossIn& loss,
                                hipStream_t st);
+// Small products (ar_gemm_small.hip), taken by the launchers above when the
+// product has at most four 256 x 256 tiles (ar_small_product): one one-wave
+// workgroup per 64 x 64 output tile, the same MFMA order per element as the
+// 256 x 256 kernels. The forward writes one partial per 64 x 64 tile
+// (ar_small_fwd_tiles of them); the float32-output product reads P block s at
+// step s < foldP and s - foldP after it, with nkP blocks per P panel.
+bool ar_small_product(int64_t rowsP, int64_t rowsQ);
+int ar_small_fwd_tiles(int64_t Tb, int64_t N);
+ar_status ar_launch_small_fwd(const uint16_t* XB, const uint16_t* WB, const void* yB, int ydt,
+                              uint16_t* dyB, float* partials, int64_t Tb, int64_t N, int64_t K,
+                              hipStream_t st);
+ar_status ar_launch_small_f32out(const uint16_t* P, const uint16_t* Q, float* out, int64_t N,
+                                 int64_t K, int64_t nkb, float scale, const ArLossIn& loss,
+                                 int64_t nkP, int64_t foldP, hipStream_t st);
 // Y[M, N] = XB·WBᵀ (XB rows M, WB rows N, reduction K), row-major f32 or bf16.
 ar_status ar_launch_gemm_out(const uint16_t* XB, const uint16_t* WB, void* Y, int ydt, int64_t M,
                              int64_t N, int64_t K, hipStream_t st);
