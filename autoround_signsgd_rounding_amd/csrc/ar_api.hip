@@ -987,8 +987,11 @@ ar_status ar_dequant_gemm(int32_t bits, int32_t group_size, const uint16_t* X, i
                                   arblk::BLOCK_ELEMS * 2);
   const int64_t nkb = arblk::k_blocks(K);
   AR_TRY(ar_launch_block_copy(X, XB, 1, M, K, nkb, st));
-  AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(WB),
-                            0.0f, arblk::row_tiles(N) * nkb * arblk::BLOCK_ELEMS / 2, st));
+  // the dequantization writes every element of [N, K]; only padding rows and
+  // reduction elements need clearing
+  if (N % arblk::ROWS != 0 || K % arblk::KB != 0)
+    AR_TRY(ar_launch_fill_f32(reinterpret_cast<float*>(WB),
+                              0.0f, arblk::row_tiles(N) * nkb * arblk::BLOCK_ELEMS / 2, st));
   AR_TRY(ar_launch_dequant_blocked(bits, qweight, qzeros, scale, N, K, (int)g, WB, st));
   return ar_launch_gemm_out(XB, WB, Y, ydt, M, N, K, st);
 }

@@ -75,6 +75,29 @@ def test_dequant_gemm_parity(M, N, K, bits, g, sym, out):
         assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(ref).max())
 
 
+@pytest.mark.parametrize("N,K", [(256, 512), (320, 520)])
+def test_prefill_with_a_dirty_workspace(N, K):
+    """The MFMA path (M > 16) in a workspace whose every byte is 0xFF (NaN as
+    bf16): with whole tiles (N % 256 == 0, K % 32 == 0) the dequantization
+    writes every element of the blocked operand; with ragged ones its padding
+    is cleared first. Either way the product equals the oracle's."""
+    M, bits, g = 40, 4, 40 if K % 40 == 0 else 128
+    if K % g:
+        g = 8
+    qw, qz, scale = _packed(N, K, bits, g, False, seed=N + K)
+    rng = np.random.default_rng(K)
+    Xb = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(F32))
+    ws = torch.full((ar.dequant_gemm_workspace_size(bits, g, M, N, K),), 255, dtype=torch.uint8,
+                    device=dev())
+    Y = ar.dequant_gemm(bf16_dev(Xb), _gpu_i32(qw), _gpu_i32(qz),
+                        torch.from_numpy(scale).to(dev()), bits, g, N, workspace=ws)
+    torch.cuda.synchronize()
+    ref = O.dequant_matmul(synth.bf16_bits_to_f32(Xb), qw, qz, scale, bits, g, N, K)
+    got = to_np(Y).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    assert rel_norm(got, ref) <= 1e-5
+
+
 def test_tuned_layer_round_trip():
     """Tune (toy 256->256, W4 g64), pack, and multiply through the packed format:
     the product equals X·bf16(Ŵ)ᵀ with the tuning loop's own Ŵ."""
