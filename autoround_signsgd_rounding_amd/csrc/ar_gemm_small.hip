@@ -46,7 +46,8 @@ struct SmallArgs {
   uint16_t* dyB;
   float* partials;     // one per 64 x 64 tile, at its tile index
   int nkbT;
-  // gradient: G [N, K] row-major, scaled; the previous forward's loss in workgroup 0
+  // float32 output: G [N, K] row-major, scaled; the previous forward's loss, reduced
+  // by the launch's last workgroup
   float* G;
   int64_t N, K;
   float scale;
