@@ -8,6 +8,7 @@ factors, plus the whole loss trajectory and the best step.
     python tests/golden/make_golden.py llama7b_q_proj          # ~15 min on 8 cores
     python tests/golden/make_golden.py llama7b_q_proj --gram   # the oracle's Gram mode
     python tests/golden/make_golden.py --block                 # Llama-7B-shaped block, see below
+    python tests/golden/make_golden.py qwen72b_up_proj --short # 8 iterations on 4 minibatches
 """
 import os
 import sys
@@ -29,8 +30,16 @@ def sample_rows(N):
     return np.sort(np.random.default_rng(ROW_SEED).choice(N, size=min(N_ROWS, N), replace=False))
 
 
-def main(name, gram=False):
+# A short run of a layer too large for the oracle's 200 iterations: the first
+# SHORT_NSAMPLES samples (SHORT_NSAMPLES / batch_samples minibatches), cycled
+# for SHORT_ITERS iterations.
+SHORT_NSAMPLES, SHORT_ITERS = 32, 8
+
+
+def main(name, gram=False, short=False):
     w = synth.WORKLOADS[name]
+    if short:
+        w = synth.Workload(**{**w.__dict__, "nsamples": SHORT_NSAMPLES, "iters": SHORT_ITERS})
     t0 = time.time()
     case = synth.make_workload_case(w)
     Y = synth.reference_outputs(case)
@@ -53,7 +62,7 @@ def main(name, gram=False):
     res = O.tune_linear(case.W, minibatch, nb, cfg, on_step=on_step, gram=gram)
     rtn_codes, _, _, _ = O.rtn_quant(case.W, cfg)
     rows = sample_rows(w.N)
-    tag = "tune_gram_" if gram else "tune_"
+    tag = "tune_gram_" if gram else ("tune_short_" if short else "tune_")
     out = os.path.join(os.path.dirname(os.path.abspath(__file__)), f"{tag}{name}.npz")
     np.savez_compressed(
         out, rows=rows, losses=np.array(res.losses, np.float64),
@@ -108,4 +117,5 @@ if __name__ == "__main__":
     if "--block" in sys.argv:
         main_block()
     else:
-        main(args[0] if args else "llama7b_q_proj", gram="--gram" in sys.argv)
+        main(args[0] if args else "llama7b_q_proj", gram="--gram" in sys.argv,
+             short="--short" in sys.argv)

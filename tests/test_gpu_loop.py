@@ -153,6 +153,37 @@ def test_200_iters_against_oracle_golden(name):
     assert agree >= 0.999
 
 
+def test_short_loop_72b_against_oracle_golden():
+    """The Qwen2.5-72B up_proj layer (8192->29568 W4 g128 asym), too large for
+    the oracle's 200 iterations: its first 32 samples (4 minibatches of 8x2048
+    tokens), 8 iterations (each minibatch twice), against the oracle's run of
+    the same problem stored by tests/golden/make_golden.py --short. Every step's
+    loss within 1e-3, the same best step, and the codes of 128 sampled rows at
+    least 99.9% identical."""
+    path = os.path.join(GOLDEN, "tune_short_qwen72b_up_proj.npz")
+    if not os.path.exists(path):
+        pytest.skip("golden file not generated")
+    gold = np.load(path)
+    w0 = synth.WORKLOADS["qwen72b_up_proj"]
+    w = synth.Workload(**{**w0.__dict__, "nsamples": 32, "iters": 8})
+    log("tune_linear qwen72b_up_proj, 32 samples, 8 iters: generating inputs")
+    case = synth.make_workload_case(w)
+    Xd = bf16_dev(case.X_bits)
+    Yd = synth.reference_outputs_torch(case, dev())
+    del case.X_bits
+    out = ar.tune_linear(weight_dev(case), Xd, Yd, _cfg(w))
+    torch.cuda.synchronize()
+    losses = to_np(out.losses).astype(np.float64)
+    gl = gold["losses"]
+    rows = torch.from_numpy(gold["rows"]).to(dev())
+    agree = np.mean(to_np(out.codes[rows]) == gold["codes"])
+    log(f"  losses {losses}\n  oracle {gl}\n  best step {int(losses.argmin())} vs "
+        f"{int(gold['best_step'])}; sampled-row codes agree {agree:.6f}")
+    assert np.all(np.abs(losses - gl) <= 1e-3 * gl)
+    assert int(losses.argmin()) == int(gold["best_step"])
+    assert agree >= 0.999
+
+
 @pytest.mark.parametrize("every", [1, 3, 40])
 def test_timed_mode_samples_steps_and_changes_nothing(every):
     """Event timing on every `every`-th step: the step count is ceil(iters /
