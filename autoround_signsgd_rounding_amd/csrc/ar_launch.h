@@ -65,10 +65,11 @@ ar_status ar_launch_gemm_wgrad(const uint16_t* dyB, const uint16_t* XTB, float* 
                                hipStream_t st);
 // Small products (ar_gemm_small.hip), taken by the launchers above when the
 // product has at most four 256 x 256 tiles (ar_small_product): one one-wave
-// workgroup per 64 x 64 output tile, the same MFMA order per element as the
-// 256 x 256 kernels. The forward writes one partial per 64 x 64 tile
-// (ar_small_fwd_tiles of them); the float32-output product reads P block s at
-// step s < foldP and s - foldP after it, with nkP blocks per P panel.
+// workgroup per 64 x 64 output tile (32 x 32 for the smallest products), the
+// same MFMA order per element as the 256 x 256 kernels. The forward writes one
+// partial per tile (ar_small_fwd_tiles of them); the float32-output product
+// reads P block s at step s < foldP and s - foldP after it, with nkP blocks per
+// P panel.
 bool ar_small_product(int64_t rowsP, int64_t rowsQ);
 int ar_small_fwd_tiles(int64_t Tb, int64_t N);
 ar_status ar_launch_small_fwd(const uint16_t* XB, const uint16_t* WB, const void* yB, int ydt,
