@@ -50,6 +50,14 @@ CASES = [
     (1, 256, 256, 2, 8, False, "f32"),
     (7, 520, 200, 8, 40, False, "f32"),
     (16, 300, 1024, 4, -1, True, "bf16"),
+    # wider layers: a K tail past the last whole step (K = 1000), each width,
+    # bf16 output, a column count that is not a multiple of 4 (per-column
+    # loads), one group per row
+    (1, 2048, 1000, 4, 40, False, "f32"),
+    (3, 2304, 512, 2, 64, False, "bf16"),
+    (2, 2049, 768, 3, 128, True, "f32"),
+    (1, 4096, 2048, 8, -1, True, "f32"),
+    (8, 2048, 1024, 4, 128, True, "bf16"),
 ]
 
 
@@ -136,10 +144,12 @@ def test_dequant_gemm_q_proj_shape(M):
     assert err <= 1e-5
 
 
-def test_decode_product_under_graph_capture():
-    """The small-M path captured in a HIP graph: every replay (with eager work
-    and synchronizations between replays) equals the eager result bit for bit."""
-    N, K, M = 512, 1024, 8
+@pytest.mark.parametrize("N", [512, 4096])
+def test_decode_product_under_graph_capture(N):
+    """The small-M path (split-K slices, then their sum in a second launch)
+    captured in a HIP graph, at two widths: every replay (with eager work and
+    synchronizations between replays) equals the eager result bit for bit."""
+    K, M = 1024, 8
     qw, qz, scale = _packed(N, K, 4, 128, False, seed=99)
     rng = np.random.default_rng(5)
     Xd = bf16_dev(synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(F32)))
