@@ -453,7 +453,10 @@ ar_status scratch_of_current_device(void** out) {
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     void* p = nullptr;
-    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return AR_ERR_HIP;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();   // leave no error behind for the caller's next HIP call
+      return AR_ERR_HIP;
+    }
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
