@@ -338,9 +338,7 @@ ar_status stage_gram_minibatch(const GramWs& w, const GramSizes& q, int64_t N, i
   // H = X_bᵀ·X_b, then its hi/lo operand [H_hi | H_lo | H_hi]
   ArLossIn none{};
   AR_TRY(ar_launch_gemm_f32out(XTBb, XTBb, w.F, K, K, nkbT, 1.0f, none, st));
-  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkbH, 0, 0, st));
-  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkbH, q.Kp, 1, st));
-  AR_TRY(ar_launch_place(w.F, AR_F32, K, K, HBb, q.nkbH, 2 * q.Kp, 0, st));
+  AR_TRY(ar_launch_place_h(w.F, K, HBb, q.nkbH, q.Kp, st));
   return AR_OK;
 }
 

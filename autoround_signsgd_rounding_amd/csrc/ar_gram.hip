@@ -367,7 +367,32 @@ ar_status ste_gram_make(const ArGramArgs& s, hipStream_t st) {
   return last_status();
 }
 
+// H [K, K] float32 into its operand [H_hi | H_lo | H_hi] (rows K, nkb blocks,
+// parts Kp apart) in one pass: each element read once, its three bf16 values
+// written where k_place's three launches would put them.
+__global__ __launch_bounds__(NT) void k_place_h(const float* __restrict__ H, uint16_t* __restrict__ dst,
+                                                int64_t K, int64_t nkb, int64_t Kp) {
+  const int64_t cpr = K / 8;
+  const int64_t total = K * cpr;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < total; i += (int64_t)gridDim.x * NT) {
+    const int64_t r = i / cpr, k = (i - r * cpr) * 8;
+    float v[8], l[8];
+    load8(H + r * K + k, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) l[e] = v[e] - bf16_val(bf16_bits(v[e]));
+    store8(dst + arblk::chunk_offset(r, k, nkb), v);
+    store8(dst + arblk::chunk_offset(r, Kp + k, nkb), l);
+    store8(dst + arblk::chunk_offset(r, 2 * Kp + k, nkb), v);
+  }
+}
+
 }  // namespace
+
+ar_status ar_launch_place_h(const float* H, int64_t K, uint16_t* dst, int64_t nkb, int64_t Kp,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_place_h, dim3(grid_for(K * (K / 8))), dim3(NT), 0, st, H, dst, K, nkb, Kp);
+  return last_status();
+}
 
 int64_t ar_gram_partials(int64_t N, int64_t K, int g) {
   int lpg, E;

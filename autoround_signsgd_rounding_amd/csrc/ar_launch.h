@@ -152,6 +152,11 @@ ar_status ar_launch_dq_gemv(int bits, const int32_t* qweight, const int32_t* qze
 // at reduction offset k_off; lo = 0: bf16(x), lo = 1: bf16(x - bf16(x)).
 ar_status ar_launch_place(const void* src, int src_dt, int64_t R, int64_t C, uint16_t* dst,
                           int64_t nkb, int64_t k_off, int lo, hipStream_t st);
+// H [K, K] float32 row-major (K % 8 == 0) into [H_hi | H_lo | H_hi] at reduction
+// offsets 0, Kp and 2·Kp of dst (nkb blocks): the three ar_launch_place calls
+// in one pass.
+ar_status ar_launch_place_h(const float* H, int64_t K, uint16_t* dst, int64_t nkb, int64_t Kp,
+                            hipStream_t st);
 // D operand of the state (V, A, B).
 ar_status ar_launch_gram_d(int wdt, const void* W, const float* V, const float* A, const float* B,
                            int64_t N, int64_t K, int g, ArGrid gr, uint16_t* DB, hipStream_t st);
